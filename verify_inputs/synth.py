@@ -1,0 +1,279 @@
+"""Seeded synthetic inputs for speculative-verify MLA attention.
+
+This module only draws random data and lays it out; it contains none of the
+attention arithmetic.  Both the CPU oracle (``oracle/``) and the HIP path use
+it, so that both sides see the same bytes.
+
+Workloads (the shapes follow the verify groups and capture buckets described
+in "Kimi K3 support with DSpark speculative decoding", section "What does this
+PR do?": draft schedule {16: 7, 32: 4, 64: 0}; the per-token bounds follow the
+"Per-token primitive" paragraph of "Kimi K3: DSpark speculative decoding under
+Helix CP"):
+
+  1  tiny verify      B=1,  H=8,  T=4,  ctx=256 (4 pages, permuted), gated
+  2  TP8 share        B=16, H=8,  T=8,  ctx ~ U{1024..1536}, pool 4096 pages
+  3  split 4          B=32, H=8,  T=5,  ctx ~ U{1024..1536}, pool 4096, S=4
+  4  plain decode     B=64, H=64, T=1,  ctx ~ U{1024..1536}, pool 4096
+  5  ragged, gated    B=64, H=64, T=8,  ctx ~ round(exp U[ln 128, ln 8192]),
+                      pool 16384, 10% of tokens bound 0, 10% truncated, S=8
+
+Conventions:
+  * bf16 tensors are numpy ``uint16`` bit patterns (round-to-nearest-even
+    from float32).
+  * ``ctx`` counts the cache including the group's own k+1 tokens, so token t
+    of a group of T sees ``ctx - (T-1) + t`` keys.
+  * Unreferenced pool pages and cache slots past a request's last visible key
+    hold a quiet NaN (0x7FC0); block-table entries past a request's pages are
+    -1.  A correct kernel never lets them reach an output.
+  * Draw order (fixed): ctx -> bounds -> page assignment -> q_nope -> W_UK ->
+    W_UV -> gate -> latent values of referenced pages -> (optional) direct
+    q_latent.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+LATENT = 512          # latent rank of the compressed KV
+PAGE = 64             # tokens per KV page
+NOPE = 128            # per-head q_nope / value dim
+BF16_NAN = np.uint16(0x7FC0)
+
+CONFIG_SEEDS = {1: 0, 2: 1, 3: 2, 4: 3, 5: 4}
+
+
+@dataclasses.dataclass
+class ConfigSpec:
+    batch: int
+    heads: int
+    q_len: int
+    pool_pages: int
+    max_pages: int          # block-table row stride
+    ctx: str                # "fixed256", "uniform", "loguniform"
+    splits: int             # 0 = library's choice
+    gated: bool
+    zero_frac: float = 0.0
+    trunc_frac: float = 0.0
+
+
+CONFIGS = {
+    1: ConfigSpec(1, 8, 4, 4, 4, "fixed256", 1, True),
+    2: ConfigSpec(16, 8, 8, 4096, 24, "uniform", 0, False),
+    3: ConfigSpec(32, 8, 5, 4096, 24, "uniform", 4, False),
+    4: ConfigSpec(64, 64, 1, 4096, 24, "uniform", 0, False),
+    5: ConfigSpec(64, 64, 8, 16384, 128, "loguniform", 8, True, 0.1, 0.1),
+}
+
+
+@dataclasses.dataclass
+class VerifyInputs:
+    """One verify batch.  bf16 arrays are uint16 bit patterns."""
+    q_nope: np.ndarray       # [B, T, H, 128] bf16
+    w_uk: np.ndarray         # [H, 128, 512] bf16
+    w_uv: np.ndarray         # [H, 128, 512] bf16
+    gate: np.ndarray         # [B, T, H, 128] bf16
+    pool: "SparsePool"       # [N_pool, 64, 512] bf16 (referenced pages stored)
+    block_table: np.ndarray  # [B, max_pages] int32, -1 past a request's pages
+    kv_bounds: np.ndarray    # [B, T] int32 visible-key counts
+    ctx: np.ndarray          # [B] int64 tokens in each request's cache
+    sm_scale: float
+    num_splits: int
+    gated: bool
+    q_latent: np.ndarray | None = None   # [B, T, H, 512] bf16, direct draw
+
+    @property
+    def shape(self):
+        b, t, h, _ = self.q_nope.shape
+        return b, t, h
+
+
+class SparsePool:
+    """A [num_pages, 64, 512] bf16 page pool of which only referenced pages are
+    stored; every other page reads as NaN.  Indexing with an integer page-id
+    array returns the dense pages, like a numpy array would."""
+
+    def __init__(self, num_pages: int, page_ids: np.ndarray, pages: np.ndarray):
+        self.num_pages = int(num_pages)
+        self.page_ids = np.asarray(page_ids, dtype=np.int64)
+        self.pages = pages
+        self.slot = np.full(self.num_pages, -1, dtype=np.int64)
+        self.slot[self.page_ids] = np.arange(self.page_ids.size)
+        self.shape = (self.num_pages, PAGE, LATENT)
+        self.dtype = np.dtype(np.uint16)
+
+    def __getitem__(self, idx):
+        idx = np.asarray(idx, dtype=np.int64)
+        if np.any((idx < 0) | (idx >= self.num_pages)):
+            raise IndexError("page id outside the pool")
+        s = self.slot[idx]
+        out = np.full(idx.shape + (PAGE, LATENT), BF16_NAN, dtype=np.uint16)
+        have = s >= 0
+        out[have] = self.pages[s[have]]
+        return out
+
+    def dense(self) -> np.ndarray:
+        out = np.full(self.shape, BF16_NAN, dtype=np.uint16)
+        out[self.page_ids] = self.pages
+        return out
+
+    def remap(self, perm: np.ndarray) -> "SparsePool":
+        """The same pages stored at ids ``perm[old_id]``."""
+        return SparsePool(self.num_pages, np.asarray(perm)[self.page_ids], self.pages)
+
+
+def f32_to_bf16_bits(x) -> np.ndarray:
+    """Round float32 values to bf16 (nearest-even) and return the bit pattern."""
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    u = x.view(np.uint32)
+    # uint32 wrap-around only happens for NaN inputs, which are overwritten below
+    rounded = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    out = rounded.astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        out[nan] = BF16_NAN
+    return out
+
+
+def bf16_bits_to_f32(u) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to float32 (data plumbing only)."""
+    u = np.ascontiguousarray(np.asarray(u, dtype=np.uint16))
+    return (u.astype(np.uint32) << 16).view(np.float32)
+
+
+def _normal_bf16(rng, shape, std):
+    return f32_to_bf16_bits((rng.standard_normal(shape) * std).astype(np.float32))
+
+
+def _draw_ctx(rng, spec: ConfigSpec) -> np.ndarray:
+    if spec.ctx == "fixed256":
+        return np.full(spec.batch, 256, dtype=np.int64)
+    if spec.ctx == "uniform":
+        return rng.integers(1024, 1536, size=spec.batch, endpoint=True).astype(np.int64)
+    if spec.ctx == "loguniform":
+        u = rng.uniform(math.log(128), math.log(8192), size=spec.batch)
+        return np.rint(np.exp(u)).astype(np.int64)
+    raise ValueError(spec.ctx)
+
+
+def _draw_bounds(rng, spec: ConfigSpec, ctx: np.ndarray) -> np.ndarray:
+    b, t = spec.batch, spec.q_len
+    causal = ctx[:, None] - (t - 1) + np.arange(t)[None, :]
+    bounds = causal.copy()
+    n_tok = b * t
+    if spec.zero_frac > 0:
+        n_zero = int(round(spec.zero_frac * n_tok))
+        zero_idx = rng.choice(n_tok, size=n_zero, replace=False)
+        bounds.reshape(-1)[zero_idx] = 0
+    if spec.trunc_frac > 0:
+        n_trunc = int(round(spec.trunc_frac * n_tok))
+        flat = bounds.reshape(-1)
+        cand = np.array([i for i in range(n_tok) if (i % t) >= 1 and flat[i] != 0])
+        pick = rng.choice(cand, size=min(n_trunc, cand.size), replace=False)
+        for i in np.sort(pick):
+            bi, ti = divmod(int(i), t)
+            earlier = int(rng.integers(0, ti))
+            flat[i] = causal[bi, earlier]
+    return bounds.astype(np.int32)
+
+
+def _assign_pages(rng, pool_pages, max_pages, n_pages):
+    total = int(n_pages.sum())
+    if total > pool_pages:
+        raise ValueError(f"{total} pages requested from a pool of {pool_pages}")
+    if int(n_pages.max(initial=0)) > max_pages:
+        raise ValueError("a request needs more pages than the block-table stride")
+    picks = rng.choice(pool_pages, size=total, replace=False).astype(np.int32)
+    table = np.full((n_pages.size, max_pages), -1, dtype=np.int32)
+    off = 0
+    for b, n in enumerate(n_pages):
+        table[b, :n] = picks[off:off + n]
+        off += n
+    return table
+
+
+def build_inputs(*, batch, heads, q_len, ctx, bounds=None, pool_pages=None, max_pages=None,
+                 seed=0, gated=True, num_splits=0, q_scale=1.0, latent_q=False,
+                 sm_scale=None, permute_single=False) -> VerifyInputs:
+    """General builder used by the named workloads and by small test cases.
+
+    ``ctx`` is an int array [B]; ``bounds`` an int array [B, T] (defaults to
+    the causal group bounds ctx-(T-1)+t).  Pages needed per request are
+    ceil(max(bounds[b]) / 64); only those are referenced.
+    """
+    rng = np.random.default_rng(seed)
+    ctx = np.asarray(ctx, dtype=np.int64).reshape(batch)
+    if bounds is None:
+        bounds = (ctx[:, None] - (q_len - 1) + np.arange(q_len)[None, :]).astype(np.int32)
+    bounds = np.asarray(bounds, dtype=np.int32).reshape(batch, q_len)
+    return _finish(rng, batch, heads, q_len, ctx, bounds, pool_pages, max_pages, gated,
+                   num_splits, q_scale, latent_q, sm_scale, permute_single)
+
+
+def _finish(rng, batch, heads, q_len, ctx, bounds, pool_pages, max_pages, gated, num_splits,
+            q_scale, latent_q, sm_scale, permute_single=False):
+    n_keys = np.clip(bounds.max(axis=1), 0, None).astype(np.int64)
+    n_pages = (n_keys + PAGE - 1) // PAGE
+    if max_pages is None:
+        max_pages = max(1, int(n_pages.max(initial=0)))
+    if pool_pages is None:
+        pool_pages = max(1, int(n_pages.sum()) * 2)
+    if permute_single:
+        # the tiny workload: block_table is a random permutation of the pool
+        assert batch == 1 and int(n_pages[0]) == pool_pages == max_pages
+        table = rng.permutation(pool_pages).astype(np.int32)[None, :]
+    else:
+        table = _assign_pages(rng, pool_pages, max_pages, n_pages)
+    std = 1.0 / math.sqrt(LATENT)
+    q_nope = _normal_bf16(rng, (batch, q_len, heads, NOPE), std * q_scale)
+    w_uk = _normal_bf16(rng, (heads, NOPE, LATENT), std)
+    w_uv = _normal_bf16(rng, (heads, NOPE, LATENT), std)
+    gate = _normal_bf16(rng, (batch, q_len, heads, NOPE), 1.0)
+    ids, pages = [], []
+    for b in range(batch):
+        n = int(n_keys[b])
+        if n == 0:
+            continue
+        vals = _normal_bf16(rng, (n, LATENT), std)
+        npg = int(n_pages[b])
+        padded = np.full((npg * PAGE, LATENT), BF16_NAN, dtype=np.uint16)
+        padded[:n] = vals
+        ids.append(table[b, :npg])
+        pages.append(padded.reshape(npg, PAGE, LATENT))
+    pool = SparsePool(pool_pages,
+                      np.concatenate(ids) if ids else np.zeros(0, np.int32),
+                      np.concatenate(pages) if pages else np.zeros((0, PAGE, LATENT), np.uint16))
+    q_latent = None
+    if latent_q:
+        # direct draw with the spread an absorbed query has (std sqrt(128)/512)
+        q_latent = _normal_bf16(rng, (batch, q_len, heads, LATENT),
+                                math.sqrt(NOPE) / LATENT * q_scale)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(NOPE)
+    return VerifyInputs(q_nope, w_uk, w_uv, gate, pool, table, bounds.astype(np.int32), ctx,
+                        float(sm_scale), int(num_splits), bool(gated), q_latent)
+
+
+# Factor on q_nope that makes the scaled scores' spread about 3 (instead of
+# ~0.002 for the stated N(0,1)/sqrt(512) draws), so softmax is far from uniform.
+SHARP_Q_SCALE = 1536.0
+
+
+def make_config(n: int, seed: int | None = None, *, sharp: bool = False,
+                latent_q: bool = False) -> VerifyInputs:
+    """One of the five named workloads, drawn from ``seed`` (default: its own)."""
+    spec = CONFIGS[n]
+    rng = np.random.default_rng(CONFIG_SEEDS[n] if seed is None else seed)
+    ctx = _draw_ctx(rng, spec)
+    bounds = _draw_bounds(rng, spec, ctx)
+    return _finish(rng, spec.batch, spec.heads, spec.q_len, ctx, bounds, spec.pool_pages,
+                   spec.max_pages, spec.gated, spec.splits,
+                   SHARP_Q_SCALE if sharp else 1.0, latent_q, None,
+                   permute_single=(spec.ctx == "fixed256"))
+
+
+def referenced_kv_bytes(inp: VerifyInputs) -> int:
+    """Bytes of KV a kernel must read: 1 KiB per visible key of each request."""
+    n = np.clip(inp.kv_bounds.max(axis=1), 0, inp.block_table.shape[1] * PAGE)
+    return int(n.sum()) * LATENT * 2
