@@ -1,0 +1,277 @@
+#!/usr/bin/env python3
+"""Benchmark: speculative-verify attention (gated NoPE MLA, absorbed) on one MI355X.
+
+A step is one verify call over one batch of the TP8-share workload (16
+requests, 8 heads, k = 7 draft tokens so q_len 8, 512-d bf16 latent cache,
+contexts uniform in [1024, 1536], 64-token pages scattered in a 4096-page
+pool).  Inputs are resident in HBM when timing starts.  To keep the 256 MB
+Infinity Cache from serving the KV, consecutive steps rotate over enough
+identical copies of the page pool (each at its own address) that the bytes
+one cycle touches exceed twice the cache ("cold").  --warm uses one copy.
+
+Prints one JSON line.  ``roofline`` is for the attention call (attention
+kernel plus the split combine when there is one): algorithmic bytes per call
+over the average call duration measured with HIP events on the launch stream.
+``cpu_baseline`` times the float64 CPU oracle on a bounded sample of the same
+workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "verify tokens/s + % of binding roofline (HBM GB/s or bf16 MFMA) on 1 MI355X"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
+MALL_BYTES = 256 << 20
+
+WORKLOAD_NAMES = {
+    1: "tiny verify B=1 H=8 q_len=4 ctx=256 gated",
+    2: "tp8-share verify B=16 H=8 q_len=8 ctx~U[1024,1536] pool=4096x64",
+    3: "verify B=32 H=8 q_len=5 ctx~U[1024,1536] split-KV 4",
+    4: "plain decode B=64 H=64 q_len=1 ctx~U[1024,1536]",
+    5: "ragged gated verify B=64 H=64 q_len=8 ctx~logU[128,8192] 10% zero 10% truncated S=8",
+}
+
+
+def algorithmic(x, gated):
+    """Bytes and flops the method must move/do per call (visible keys only)."""
+    import numpy as np
+    b, t, h = x.shape
+    r = t * h
+    max_keys = x.block_table.shape[1] * 64
+    bounds = np.clip(x.kv_bounds, 0, max_keys)
+    n_b = bounds.max(axis=1)
+    kv = int(n_b.sum()) * 512 * 2
+    q = b * r * 512 * 2
+    lse = b * r * 4
+    tables = int(((n_b + 63) // 64).sum()) * 4 + b * t * 4
+    if gated:
+        out = b * r * 128 * 2
+        extra = h * 128 * 512 * 2 + b * r * 128 * 2      # W_UV + gate
+    else:
+        out = b * r * 512 * 2
+        extra = 0
+    flops = 4 * 512 * int(bounds.sum()) * h
+    if gated:
+        flops += 2 * 512 * 128 * b * r
+    return {"kv_bytes": kv, "bytes": kv + q + lse + tables + out + extra, "flops": flops}
+
+
+def cpu_baseline(x, seconds):
+    """Time the float64 oracle (latent definition of the call) on whole batches
+    of the same workload until ~`seconds` of CPU time, at least once."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    q_bits = oracle_q_bits(x)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.verify_attention_latent(q_bits, x.pool, x.block_table, x.kv_bounds, x.sm_scale)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 50:
+            break
+    b, t, _ = x.shape
+    return {"value": round(reps * b * t / el, 3), "unit": "verify tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{reps} full batch(es) of the timed workload through the float64 NumPy "
+                      f"oracle (latent definition), {el:.1f} s wall"}
+
+
+def oracle_q_bits(x):
+    import oracle
+    from verify_inputs import f32_to_bf16_bits
+    import numpy as np
+    return f32_to_bf16_bits(oracle.absorb_query(x.q_nope, x.w_uk).astype(np.float32))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--splits", type=int, default=None, help="force num_splits (0 = library)")
+    ap.add_argument("--eager", action="store_true", help="time eager launches, not graph replay")
+    ap.add_argument("--warm", action="store_true", help="one pool copy (cache-warm)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        if int(os.environ.get("RANK", "0")) == 0:
+            print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
+                  f"{world}); this verify-attention path does not shard across GPUs.",
+                  file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import speculative_verify_attention_absorbed_amd as mv
+    from verify_inputs import make_config
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = mv.load_library()
+
+    x = make_config(args.config)
+    b, t, h = x.shape
+    gated = x.gated
+    splits = x.num_splits if args.splits is None else args.splits
+    alg = algorithmic(x, gated)
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ---- device inputs (HBM resident before timing)
+    ids = torch.from_numpy(x.pool.page_ids.astype(np.int64)).to(dev)
+    pages = up(x.pool.pages)
+    n_sets = 1 if args.warm else max(2, min(64, math.ceil(2 * MALL_BYTES / max(alg["kv_bytes"], 1))))
+    pools = []
+    for _ in range(n_sets):
+        p = torch.full((x.pool.num_pages, 64, 512), float("nan"), dtype=torch.bfloat16, device=dev)
+        p[ids] = pages
+        pools.append(p)
+    bt = torch.from_numpy(x.block_table).to(dev)
+    bounds = torch.from_numpy(x.kv_bounds).to(dev)
+    q_lat = mv.verify_absorb_q(up(x.q_nope), up(x.w_uk))     # HIP absorption, outside the timing
+    w_uv = up(x.w_uv)
+    gate = up(x.gate)
+    params = mv.VerifyParams.make(b, t, h, x.block_table.shape[1], x.pool.num_pages, x.sm_scale,
+                                  splits)
+    s_used = mv.verify_num_splits(params, gated)
+    ws_bytes = mv.verify_workspace_size(params, gated)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    if gated:
+        out = torch.empty((b, t, h, 128), dtype=torch.bfloat16, device=dev)
+    else:
+        out = torch.empty((b, t, h, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((b, t, h), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    vp = ctypes.c_void_p
+    pref = ctypes.byref(params)
+
+    def call(i, stream_handle):
+        pool = pools[i % n_sets]
+        if gated:
+            rc = lib.mla_verify_attn_gated(pref, vp(q_lat.data_ptr()), vp(pool.data_ptr()),
+                                           vp(bt.data_ptr()), vp(bounds.data_ptr()),
+                                           vp(w_uv.data_ptr()), vp(gate.data_ptr()),
+                                           vp(out.data_ptr()), vp(lse.data_ptr()), vp(0),
+                                           vp(ws.data_ptr()), ctypes.c_size_t(ws_bytes),
+                                           stream_handle)
+        else:
+            rc = lib.mla_verify_attn(pref, vp(q_lat.data_ptr()), vp(pool.data_ptr()),
+                                     vp(bt.data_ptr()), vp(bounds.data_ptr()), vp(out.data_ptr()),
+                                     vp(lse.data_ptr()), vp(ws.data_ptr()),
+                                     ctypes.c_size_t(ws_bytes), stream_handle)
+        if rc != 0:
+            raise mv.MlaVerifyError(rc, "bench call")
+
+    stream = torch.cuda.current_stream()
+    sh = vp(stream.cuda_stream)
+    for i in range(max(args.warmup, 1)):
+        call(i, sh)
+    torch.cuda.synchronize()
+
+    mode = "eager"
+    graph = None
+    if not args.eager:
+        # capture one rotation cycle (n_sets calls, at least 8) and replay it
+        per_graph = n_sets * max(1, math.ceil(8 / n_sets))
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                csh = vp(torch.cuda.current_stream().cuda_stream)
+                for i in range(per_graph):
+                    call(i, csh)
+        stream.wait_stream(cap)
+        torch.cuda.synchronize()
+        graph = (g, per_graph)
+        mode = f"hipGraph replay ({per_graph} calls per graph)"
+        for _ in range(max(1, args.warmup // per_graph)):
+            g.replay()
+        torch.cuda.synchronize()
+
+    # ---- timed region: exactly `steps` calls
+    steps = args.steps
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    if graph is None:
+        start.record(stream)
+        for i in range(steps):
+            call(i, sh)
+        end.record(stream)
+    else:
+        g, per_graph = graph
+        steps = per_graph * max(1, round(args.steps / per_graph))
+        start.record(stream)
+        for _ in range(steps // per_graph):
+            g.replay()
+        end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    sec = ms * 1e-3
+
+    tokens = b * t
+    achieved_gbs = alg["bytes"] / sec / 1e9
+    achieved_tflops = alg["flops"] / sec / 1e12
+    bound = "mfma" if args.config == 5 else "hbm"
+    if bound == "hbm":
+        roof = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        roof = {"bound": "mfma", "achieved": round(achieved_tflops, 2),
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+
+    rec = {
+        "metric": METRIC,
+        "value": round(tokens / sec, 1),
+        "unit": "verify tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_NAMES[args.config], "batch": b, "heads": h, "q_len": t,
+                   "num_splits": s_used, "gated": gated,
+                   "cache": "warm" if args.warm else f"cold: {n_sets} rotating pool copies",
+                   "launch": mode},
+        "roofline": roof,
+        "extra": {"algorithmic_bytes": alg["bytes"], "kv_bytes": alg["kv_bytes"],
+                  "flops": alg["flops"], "attention_tflops": round(achieved_tflops, 3),
+                  "kv_gbs": round(alg["kv_bytes"] / sec / 1e9, 1),
+                  "mfma_frac": round(achieved_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                  "hbm_frac": round(achieved_gbs / HBM_PEAK_GBS, 4)},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,186 @@
+/*
+ * mla_verify.h -- C ABI of the MI355X (gfx950) speculative-verify attention
+ * library for gated NoPE MLA with absorbed projections.
+ *
+ * What is computed (sources are the pages this library follows):
+ *
+ *  - "Kimi K3 support with DSpark speculative decoding", section "What does
+ *    this PR do?": gated NoPE MLA with absorbed projections, and every decode
+ *    step turned into a verify of k drafted tokens.  A request therefore
+ *    brings a group of T = k+1 query tokens.  With absorption the per-head
+ *    query lives in the 512-d latent space (q_latent = W_UK[h]^T q_nope) and
+ *    attends directly over the compressed latent cache, which serves as both
+ *    keys and values; W_UV is applied after the attention.
+ *  - "Kimi K3: DSpark speculative decoding under Helix CP", first commit
+ *    message ("Per-token primitive", "CuTe DSL MLA decode") and "Changes":
+ *    each token of the group has its own attention bound kv_bounds[b, t] (the
+ *    number of visible keys, its position + 1), which replaces the implicit
+ *    causal bound; the softmax statistics are returned per token, and a token
+ *    with no visible key yields the (-inf, 0) identity: lse = -inf, output 0.
+ *    The third commit message of that page: such rows must never read pool
+ *    bytes (a 0 * NaN would poison the merge).
+ *  - Same page, commit on "fold_sq padding rows" and the reduction kernel:
+ *    the group's tokens are folded into the head dimension, folded row
+ *    r = t * H + h belongs to token r / H; padding rows clamp their token
+ *    index and are never stored.
+ *  - vLLM "specialized_decode.drafter.model", module docstring: the draft
+ *    block's attention folds its tokens into heads (one decode row per
+ *    request instead of one per token), and partial results are merged by an
+ *    LSE combine followed by W_UV.
+ *
+ * Per request b, token t, head h, with L = clamp(kv_bounds[b,t], 0, P*64):
+ *     s_j    = sm_scale * <q_latent[b,t,h,:], C_b[j,:]>        j < L
+ *     lse    = ln sum_j exp(s_j)                    (-inf if L == 0)
+ *     o_lat  = sum_j softmax(s)_j C_b[j,:]          (0    if L == 0)
+ *     out    = sigmoid(gate[b,t,h,:]) * (W_UV[h] o_lat)   (gated entry)
+ * where C_b[j] = latent_kv_pages[block_table[b, j/64], j%64, :].
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers, row-major, contiguous, with
+ *    the shapes given below, and 16-byte aligned.  bf16 is stored as its
+ *    16-bit pattern (mla_bf16).
+ *  - The caller owns every buffer and the stream.  The library never
+ *    allocates, frees or keeps a pointer after it returns; inputs are
+ *    read-only; outputs are fully overwritten (masked rows get 0 / -inf).
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream).  They do no host synchronisation and no device->host copy,
+ *    so they may be captured into a hipGraph.
+ *  - Results are deterministic: identical inputs give identical bits.
+ *  - Return value: MLA_OK (0) or a negative MLA_ERR_* code.  Argument
+ *    checks run on the host before any HIP call; unsupported requests fail
+ *    loudly and never fall back to another path.
+ *  - Device-side preconditions (documented, checked defensively):
+ *    kv_bounds values are clamped into [0, max_pages_per_req * 64];
+ *    block_table[b, p] must lie in [0, num_pool_pages) for every page p
+ *    below ceil(max_t bound / 64) -- other entries are never read, and an
+ *    out-of-range id is not dereferenced (its keys then read as zeros, an
+ *    undefined but fault-free result); pool slots past a request's largest
+ *    bound may hold any bytes, NaN included.
+ */
+#ifndef MLA_VERIFY_H
+#define MLA_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t mla_bf16; /* bf16 bit pattern, round-to-nearest-even */
+
+enum mla_verify_status {
+  MLA_OK = 0,
+  MLA_ERR_NULL = -1,        /* a required pointer is NULL                  */
+  MLA_ERR_SHAPE = -2,       /* latent != 512, page != 64, T/H/B out of range */
+  MLA_ERR_DTYPE = -3,       /* kv_dtype other than MLA_KV_BF16 (fp8 etc.)  */
+  MLA_ERR_ARG = -4,         /* bad sm_scale, num_splits, pool size, or a   */
+                            /* pointer that is not 16-byte aligned         */
+  MLA_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required  */
+  MLA_ERR_DEVICE = -6,      /* current device is not gfx950                */
+  MLA_ERR_HIP = -7          /* a HIP call or kernel launch failed          */
+};
+
+enum mla_verify_kv_dtype {
+  MLA_KV_BF16 = 0,
+  MLA_KV_FP8_E4M3 = 1       /* declared so callers can ask; always rejected */
+};
+
+/* Limits (MLA_ERR_SHAPE outside them). */
+#define MLA_VERIFY_LATENT 512
+#define MLA_VERIFY_PAGE 64
+#define MLA_VERIFY_NOPE 128       /* per-head value dim of W_UV / gate / out */
+#define MLA_VERIFY_MAX_Q_LEN 16
+#define MLA_VERIFY_MAX_HEADS 128
+#define MLA_VERIFY_MAX_SPLITS 64
+
+typedef struct mla_verify_params {
+  int32_t batch;             /* B >= 1 requests                              */
+  int32_t q_len;             /* T = k+1 tokens per group, 1..16              */
+  int32_t num_heads;         /* H, 1..128                                    */
+  int32_t latent_dim;        /* must be 512                                  */
+  int32_t page_size;         /* must be 64                                   */
+  int32_t max_pages_per_req; /* P, block_table row stride (>= 1)             */
+  int32_t num_pool_pages;    /* N, pages in latent_kv_pages (>= 1)           */
+  int32_t num_splits;        /* 0 = library's choice; 1..64 = forced split-KV */
+  float sm_scale;            /* softmax scale, finite and > 0                */
+  int32_t kv_dtype;          /* MLA_KV_BF16 only                             */
+} mla_verify_params;
+
+/* Validates `p` (pure host code, no HIP call).  MLA_OK or an error code. */
+int mla_verify_check(const mla_verify_params* p);
+
+/* The number of KV splits S the library will use for `p` (resolves
+ * num_splits == 0).  Pure host code.  Returns S >= 1, or an error code. */
+int mla_verify_num_splits(const mla_verify_params* p, int gated);
+
+/* Workspace bytes the call needs (0 when it needs none).  `gated` selects
+ * mla_verify_attn_gated.  Pure host code.  Layout (fp32): partial outputs
+ * [S][B*T*H][512] then partial LSEs [S][B*T*H].  Returns MLA_OK or an
+ * error code; *bytes is written only on success. */
+int mla_verify_workspace_size(const mla_verify_params* p, int gated, size_t* bytes);
+
+/* Verify attention, latent output.
+ *   q_latent        [B, T, H, 512] bf16   absorbed queries (row t*H+h = fold)
+ *   latent_kv_pages [N, 64, 512]   bf16   paged latent cache
+ *   block_table     [B, P]         int32  page ids in logical order
+ *   kv_bounds       [B, T]         int32  visible-key count per token
+ *   out_latent      [B, T, H, 512] bf16   o_lat (0 for rows with bound 0)
+ *   lse             [B, T, H]      fp32   natural-log LSE (-inf if bound 0)
+ *   workspace       mla_verify_workspace_size(p, 0) bytes, or NULL if 0
+ * Errors: MLA_ERR_NULL/SHAPE/DTYPE/ARG/WORKSPACE (host), MLA_ERR_DEVICE,
+ * MLA_ERR_HIP (launch failure, reported without synchronising). */
+int mla_verify_attn(const mla_verify_params* p,
+                    const mla_bf16* q_latent,
+                    const mla_bf16* latent_kv_pages,
+                    const int32_t* block_table,
+                    const int32_t* kv_bounds,
+                    mla_bf16* out_latent,
+                    float* lse,
+                    void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* Verify attention with the fused LSE combine + W_UV + sigmoid-gate epilogue
+ * (vLLM drafter docstring: "LSE combine + W_UV"; the gate of "gated NoPE
+ * MLA" read as an elementwise sigmoid over the 128-d per-head output).
+ *   w_uv            [H, 128, 512]  bf16   o_v[d] = sum_c W_UV[h][d][c] o_lat[c]
+ *   gate_logits     [B, T, H, 128] bf16
+ *   out             [B, T, H, 128] bf16   sigmoid(gate) * o_v
+ *   lse             [B, T, H]      fp32
+ *   out_latent      [B, T, H, 512] bf16   optional (NULL = not written)
+ *   workspace       mla_verify_workspace_size(p, 1) bytes (always > 0)
+ * Other arguments and errors as mla_verify_attn. */
+int mla_verify_attn_gated(const mla_verify_params* p,
+                          const mla_bf16* q_latent,
+                          const mla_bf16* latent_kv_pages,
+                          const int32_t* block_table,
+                          const int32_t* kv_bounds,
+                          const mla_bf16* w_uv,
+                          const mla_bf16* gate_logits,
+                          mla_bf16* out,
+                          float* lse,
+                          mla_bf16* out_latent,
+                          void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* Query absorption ("absorbed projections", first page, "What does this PR
+ * do?"): q_latent[b,t,h,:] = W_UK[h]^T q_nope[b,t,h,:], fp32 accumulation,
+ * rounded to bf16 (nearest-even).
+ *   q_nope   [B, T, H, 128] bf16,  w_uk [H, 128, 512] bf16,
+ *   q_latent [B, T, H, 512] bf16 (output).
+ * Uses batch, q_len, num_heads of `p` (other fields are validated as for
+ * the attention calls).  No workspace. */
+int mla_verify_absorb_q(const mla_verify_params* p,
+                        const mla_bf16* q_nope,
+                        const mla_bf16* w_uk,
+                        mla_bf16* q_latent,
+                        void* stream);
+
+/* Static, human-readable text for a status code. */
+const char* mla_verify_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_VERIFY_H */

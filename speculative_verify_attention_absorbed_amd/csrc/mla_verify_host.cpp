@@ -1,0 +1,98 @@
+// Host-side argument validation and planning for the verify-attention C ABI.
+// Pure C++: nothing here touches the HIP runtime, so every error path can be
+// exercised on a machine without a GPU.
+#include <cmath>
+#include <cstdint>
+
+#include "mla_verify.h"
+#include "mla_verify_internal.h"
+
+namespace mla {
+
+int check_params(const mla_verify_params* p) {
+  if (p == nullptr) return MLA_ERR_NULL;
+  if (p->kv_dtype != MLA_KV_BF16) return MLA_ERR_DTYPE;
+  if (p->latent_dim != MLA_VERIFY_LATENT || p->page_size != MLA_VERIFY_PAGE) return MLA_ERR_SHAPE;
+  if (p->batch < 1 || p->q_len < 1 || p->q_len > MLA_VERIFY_MAX_Q_LEN || p->num_heads < 1 ||
+      p->num_heads > MLA_VERIFY_MAX_HEADS)
+    return MLA_ERR_SHAPE;
+  if (p->max_pages_per_req < 1 || p->num_pool_pages < 1) return MLA_ERR_ARG;
+  // keep every index computation comfortably inside int32 / size_t
+  if ((int64_t)p->max_pages_per_req * MLA_VERIFY_PAGE > (int64_t)1 << 30) return MLA_ERR_ARG;
+  if ((int64_t)p->batch * p->max_pages_per_req > (int64_t)1 << 30) return MLA_ERR_ARG;
+  if ((int64_t)p->batch * p->q_len * p->num_heads > (int64_t)1 << 24) return MLA_ERR_SHAPE;
+  if (p->num_splits < 0 || p->num_splits > MLA_VERIFY_MAX_SPLITS) return MLA_ERR_ARG;
+  if (!std::isfinite(p->sm_scale) || !(p->sm_scale > 0.0f)) return MLA_ERR_ARG;
+  // a forced split count must keep every split within kMaxSplitPages pages
+  if (p->num_splits > 0 &&
+      (p->max_pages_per_req + p->num_splits - 1) / p->num_splits > kMaxSplitPages)
+    return MLA_ERR_ARG;
+  if ((p->max_pages_per_req + kMaxSplitPages - 1) / kMaxSplitPages > MLA_VERIFY_MAX_SPLITS)
+    return MLA_ERR_ARG;
+  return MLA_OK;
+}
+
+Plan make_plan(const mla_verify_params* p, bool gated) {
+  Plan pl{};
+  pl.rows = p->q_len * p->num_heads;
+  pl.row_tiles = (pl.rows + kTileRows - 1) / kTileRows;
+  int s = p->num_splits;
+  if (s == 0) {
+    // Library's choice: about one workgroup per compute unit (a workgroup
+    // holds ~138 KiB of LDS, so one fits per CU), and at least two pages per
+    // split, since every split writes an fp32 partial row tile.
+    const int64_t tiles = (int64_t)p->batch * pl.row_tiles;
+    int64_t want = (kNumCUs + tiles / 2) / tiles;
+    const int64_t cap = p->max_pages_per_req / 2 > 1 ? p->max_pages_per_req / 2 : 1;
+    if (want > cap) want = cap;
+    if (want > MLA_VERIFY_MAX_SPLITS) want = MLA_VERIFY_MAX_SPLITS;
+    s = want < 1 ? 1 : (int)want;
+  }
+  // one split stages at most kMaxSplitPages block-table entries
+  const int min_s = (p->max_pages_per_req + kMaxSplitPages - 1) / kMaxSplitPages;
+  if (p->num_splits == 0 && s < min_s) s = min_s;
+  pl.splits = s;
+  pl.use_partials = gated || s > 1;
+  const size_t total_rows = (size_t)p->batch * pl.rows;
+  pl.workspace_bytes =
+      pl.use_partials ? (size_t)s * total_rows * (MLA_VERIFY_LATENT + 1) * sizeof(float) : 0;
+  return pl;
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+}  // namespace mla
+
+extern "C" {
+
+int mla_verify_check(const mla_verify_params* p) { return mla::check_params(p); }
+
+int mla_verify_num_splits(const mla_verify_params* p, int gated) {
+  const int rc = mla::check_params(p);
+  if (rc != MLA_OK) return rc;
+  return mla::make_plan(p, gated != 0).splits;
+}
+
+int mla_verify_workspace_size(const mla_verify_params* p, int gated, size_t* bytes) {
+  if (bytes == nullptr) return MLA_ERR_NULL;
+  const int rc = mla::check_params(p);
+  if (rc != MLA_OK) return rc;
+  *bytes = mla::make_plan(p, gated != 0).workspace_bytes;
+  return MLA_OK;
+}
+
+const char* mla_verify_status_string(int status) {
+  switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_NULL: return "a required pointer is NULL";
+    case MLA_ERR_SHAPE: return "unsupported shape (latent must be 512, page 64, 1<=T<=16, 1<=H<=128)";
+    case MLA_ERR_DTYPE: return "unsupported KV dtype (only bf16 latent pages are supported)";
+    case MLA_ERR_ARG: return "invalid argument (sm_scale, num_splits, pool/page counts or alignment)";
+    case MLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MLA_ERR_DEVICE: return "current device is not gfx950 (MI355X)";
+    case MLA_ERR_HIP: return "HIP runtime or kernel launch error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,113 @@
+"""Helpers for the GPU parity tests: upload seeded inputs, compare results."""
+import math
+
+import numpy as np
+import torch
+
+from verify_inputs import LATENT, PAGE, VerifyInputs, f32_to_bf16_bits
+
+# acceptance bar for floating-point outputs and LSE
+MAX_ABS = 1e-2
+REL_L2 = 5e-3
+LSE_ABS = 1e-3
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def bf16_tensor(bits: np.ndarray, device=None) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+    return t.to(device or dev())
+
+
+def bits_of(t: torch.Tensor) -> np.ndarray:
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def f64_of(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def upload_pool(x: VerifyInputs, device=None) -> torch.Tensor:
+    """Dense device pool: referenced pages from the generator, NaN elsewhere."""
+    device = device or dev()
+    pool = torch.full((x.pool.num_pages, PAGE, LATENT), float("nan"), dtype=torch.bfloat16,
+                      device=device)
+    if x.pool.page_ids.size:
+        ids = torch.from_numpy(x.pool.page_ids.astype(np.int64)).to(device)
+        pool[ids] = bf16_tensor(x.pool.pages, device)
+    return pool
+
+
+def upload_dense_pool(pool_bits: np.ndarray, device=None) -> torch.Tensor:
+    return bf16_tensor(pool_bits, device)
+
+
+def upload(x: VerifyInputs, device=None, q_latent_bits=None):
+    device = device or dev()
+    d = {
+        "pool": upload_pool(x, device),
+        "block_table": torch.from_numpy(x.block_table).to(device),
+        "kv_bounds": torch.from_numpy(x.kv_bounds).to(device),
+        "q_nope": bf16_tensor(x.q_nope, device),
+        "w_uk": bf16_tensor(x.w_uk, device),
+        "w_uv": bf16_tensor(x.w_uv, device),
+        "gate": bf16_tensor(x.gate, device),
+    }
+    ql = q_latent_bits if q_latent_bits is not None else x.q_latent
+    if ql is not None:
+        d["q_latent"] = bf16_tensor(ql, device)
+    return d
+
+
+def round_bf16(a64: np.ndarray) -> np.ndarray:
+    """Host-side RNE rounding of float64 values to bf16 bits (via float32)."""
+    return f32_to_bf16_bits(np.asarray(a64, dtype=np.float32))
+
+
+def assert_close_output(got: np.ndarray, want: np.ndarray, what: str, mask_rows=None):
+    """The benchmark spec bar: max-abs <= 1e-2 and relative L2 <= 5e-3."""
+    assert got.shape == want.shape, (got.shape, want.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    diff = got - want
+    max_abs = float(np.abs(diff).max()) if diff.size else 0.0
+    denom = float(np.linalg.norm(want))
+    rel = float(np.linalg.norm(diff)) / denom if denom > 0 else float(np.linalg.norm(diff))
+    assert max_abs <= MAX_ABS, f"{what}: max abs error {max_abs:.3e}"
+    assert rel <= REL_L2, f"{what}: relative L2 error {rel:.3e}"
+    return max_abs, rel
+
+
+def assert_lse(got: np.ndarray, want: np.ndarray, what="lse"):
+    """Finite LSEs within 1e-3; masked rows exactly -inf."""
+    inf_w = np.isneginf(want)
+    assert np.array_equal(np.isneginf(got), inf_w), f"{what}: -inf pattern differs"
+    assert not np.isnan(got).any(), f"{what}: NaN"
+    fin = ~inf_w
+    if fin.any():
+        err = float(np.abs(got[fin] - want[fin]).max())
+        assert err <= LSE_ABS, f"{what}: max abs error {err:.3e}"
+
+
+def assert_masked_rows_zero(out: np.ndarray, lse_want: np.ndarray, what="out"):
+    rows = np.isneginf(lse_want)
+    if rows.any():
+        assert np.all(out[rows] == 0), f"{what}: masked rows are not exactly 0"
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def rel_l2(a, b):
+    n = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / n) if n > 0 else float(np.linalg.norm(a - b))
+
+
+def sm_scale():
+    return 1.0 / math.sqrt(128)

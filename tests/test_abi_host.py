@@ -1,0 +1,121 @@
+"""Host-side checks of the C ABI: the library loads, exports every function the
+header declares, and rejects bad arguments before any HIP call (these run
+without a GPU)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import speculative_verify_attention_absorbed_amd as mv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mv.lib_path()):
+        from speculative_verify_attention_absorbed_amd import _build
+        _build.build()
+    return mv.load_library()
+
+
+def header_functions():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(mla_\w+)\s*\(", text))
+    return sorted(names)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    declared = header_functions()
+    assert set(declared) == set(mv.EXPORTED_SYMBOLS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def good(**kw):
+    base = dict(batch=16, q_len=8, num_heads=8, max_pages_per_req=24, num_pool_pages=4096,
+                sm_scale=1 / math.sqrt(128))
+    base.update(kw)
+    return mv.VerifyParams.make(**base)
+
+
+def test_check_accepts_valid(lib):
+    assert mv.verify_check(good()) == 0
+    assert mv.verify_check(good(q_len=16, num_heads=128)) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(latent_dim=576), -2), (dict(page_size=32), -2), (dict(q_len=0), -2),
+    (dict(q_len=17), -2), (dict(num_heads=0), -2), (dict(num_heads=129), -2), (dict(batch=0), -2),
+    (dict(kv_dtype=1), -3), (dict(kv_dtype=7), -3),
+    (dict(sm_scale=0.0), -4), (dict(sm_scale=-1.0), -4), (dict(sm_scale=float("nan")), -4),
+    (dict(sm_scale=float("inf")), -4), (dict(num_splits=-1), -4), (dict(num_splits=65), -4),
+    (dict(max_pages_per_req=0), -4), (dict(num_pool_pages=0), -4),
+])
+def test_check_rejects(lib, kw, code):
+    assert mv.verify_check(good(**kw)) == code
+
+
+def test_null_params(lib):
+    assert lib.mla_verify_check(None) == -1
+    assert lib.mla_verify_workspace_size(ctypes.byref(good()), 0, None) == -1
+
+
+def test_fp8_kv_is_rejected_loudly(lib):
+    p = good(kv_dtype=mv.KV_FP8_E4M3)
+    with pytest.raises(mv.MlaVerifyError, match="MLA_ERR_DTYPE"):
+        mv.verify_workspace_size(p)
+
+
+def test_split_plan_and_workspace(lib):
+    # forced split counts are honoured; direct (unsplit, ungated) needs no workspace
+    p1 = good(num_splits=1)
+    assert mv.verify_num_splits(p1) == 1 and mv.verify_workspace_size(p1) == 0
+    rows = 16 * 8 * 8
+    p4 = good(num_splits=4)
+    assert mv.verify_num_splits(p4) == 4
+    assert mv.verify_workspace_size(p4) == 4 * rows * 513 * 4
+    # the gated path always stages partials
+    assert mv.verify_workspace_size(p1, gated=True) == rows * 513 * 4
+    # automatic choice stays within [1, max_pages/2]
+    for b, t, h, pmax in [(16, 8, 8, 24), (64, 1, 64, 24), (1, 4, 8, 4), (64, 8, 64, 128),
+                          (1, 1, 1, 1)]:
+        s = mv.verify_num_splits(good(batch=b, q_len=t, num_heads=h, max_pages_per_req=pmax))
+        assert 1 <= s <= max(1, pmax // 2)
+
+
+def test_status_strings(lib):
+    for code in range(-7, 1):
+        assert mv.status_string(code)
+    assert mv.status_string(-99) == "unknown status"
+
+
+def test_entry_points_validate_before_any_hip_call(lib):
+    """Bad arguments come back as error codes, with no device touched."""
+    p = good()
+    fake = ctypes.c_void_p(0x1000)
+    z = ctypes.c_void_p(0)
+    args = [fake] * 6
+    # NULL pointers
+    assert lib.mla_verify_attn(ctypes.byref(p), z, *args[1:], z, 0, z) == -1
+    assert lib.mla_verify_attn_gated(ctypes.byref(p), fake, fake, fake, fake, z, fake, fake, fake,
+                                     z, fake, 1 << 30, z) == -1
+    assert lib.mla_verify_absorb_q(ctypes.byref(p), z, fake, fake, z) == -1
+    # misaligned pointer
+    odd = ctypes.c_void_p(0x1002)
+    assert lib.mla_verify_attn(ctypes.byref(good(num_splits=1)), odd, *args[1:], z, 0, z) == -4
+    # workspace too small (split plan needs partials)
+    p4 = good(num_splits=4)
+    assert lib.mla_verify_attn(ctypes.byref(p4), *args, z, 0, z) == -5
+    assert lib.mla_verify_attn(ctypes.byref(p4), *args, fake, 16, z) == -5
+    assert lib.mla_verify_attn_gated(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake,
+                                     fake, z, z, 0, z) == -5
+    # bad params take precedence over everything else
+    assert lib.mla_verify_attn(ctypes.byref(good(latent_dim=576)), z, *args[1:], z, 0, z) == -2
+    assert lib.mla_verify_attn(None, *args, z, 0, z) == -1

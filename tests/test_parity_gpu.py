@@ -1,0 +1,252 @@
+"""Parity of the HIP path (through the C ABI) with the float64 CPU oracle.
+
+Every test prints the case it is about to run, then runs it on cuda:0.
+Bars: outputs max-abs <= 1e-2 and relative L2 <= 5e-3; finite LSE within
+1e-3; masked rows exactly (-inf, 0); indexing probes bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import speculative_verify_attention_absorbed_amd as mv
+from gpu_util import (assert_close_output, assert_lse, assert_masked_rows_zero, bits_of,
+                      bf16_tensor, f64_of, log, rel_l2, round_bf16, sync, upload,
+                      upload_dense_pool)
+from probes import needle_case, needle_expected
+from verify_inputs import build_inputs, make_config
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle_qlat_bits(x):
+    """The ABI input: q_latent = bf16(W_UK^T q_nope) computed in float64."""
+    return round_bf16(oracle.absorb_query(x.q_nope, x.w_uk))
+
+
+def run_latent(x, d, num_splits=None):
+    s = x.num_splits if num_splits is None else num_splits
+    out, lse = mv.verify_attn(d["q_latent"], d["pool"], d["block_table"], d["kv_bounds"],
+                              x.sm_scale, num_splits=s)
+    sync()
+    return f64_of(out), lse.cpu().numpy().astype(np.float64), out
+
+
+def check_latent(x, d, q_bits, num_splits=None, what=""):
+    got, lse, _ = run_latent(x, d, num_splits)
+    want, want_lse = oracle.verify_attention_latent(q_bits, x.pool, x.block_table, x.kv_bounds,
+                                                    x.sm_scale)
+    assert_lse(lse, want_lse, f"{what} lse")
+    assert_masked_rows_zero(got, want_lse, f"{what} out_latent")
+    return assert_close_output(got, want, f"{what} out_latent")
+
+
+# ------------------------------------------------------------------ absorption
+@pytest.mark.parametrize("cfg,sharp", [(1, False), (2, False), (2, True), (5, False)])
+def test_absorb_q_matches_oracle(cfg, sharp):
+    """fp32 accumulation then one bf16 rounding: every element lies within half
+    a bf16 ulp plus the fp32 summation bound n * 2^-24 * sum|q_d W_dc| of the
+    exact float64 value."""
+    log(f"absorb: config {cfg} sharp={sharp}")
+    x = make_config(cfg, sharp=sharp)
+    d = upload(x)
+    q = mv.verify_absorb_q(d["q_nope"], d["w_uk"])
+    sync()
+    got = f64_of(q)
+    want = oracle.absorb_query(x.q_nope, x.w_uk)
+    mag = np.einsum("bthd,hdc->bthc", np.abs(oracle.bf16_to_f64(x.q_nope)),
+                    np.abs(oracle.bf16_to_f64(x.w_uk)))
+    top = np.maximum(np.abs(got), np.abs(want))
+    ulp = np.exp2(np.floor(np.log2(np.maximum(top, 1e-38))) - 7)
+    allowed = 0.5 * ulp + 128 * 2.0 ** -24 * mag
+    excess = np.abs(got - want) - allowed
+    assert excess.max() <= 0, f"worst excess {excess.max():.3e}"
+    assert rel_l2(got, want) < 5e-3
+
+
+# ------------------------------------------------------------------ latent ABI
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+@pytest.mark.parametrize("sharp", [False, True])
+def test_latent_parity_configs(cfg, sharp):
+    log(f"latent parity: config {cfg} sharp={sharp}")
+    x = make_config(cfg, sharp=sharp)
+    q_bits = oracle_qlat_bits(x)
+    d = upload(x, q_latent_bits=q_bits)
+    check_latent(x, d, q_bits, what=f"cfg{cfg}")
+
+
+def test_latent_parity_config5_full():
+    log("latent parity: config 5 (ragged, zero and truncated bounds), S=8")
+    x = make_config(5)
+    q_bits = oracle_qlat_bits(x)
+    d = upload(x, q_latent_bits=q_bits)
+    check_latent(x, d, q_bits, what="cfg5")
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 4, 7, 8, 16])
+def test_split_invariance(splits):
+    log(f"split invariance: config 3 (sharp), S={splits}")
+    x = make_config(3, sharp=True)
+    q_bits = oracle_qlat_bits(x)
+    d = upload(x, q_latent_bits=q_bits)
+    check_latent(x, d, q_bits, num_splits=splits, what=f"S={splits}")
+
+
+@pytest.mark.parametrize("heads,q_len", [(1, 1), (8, 9), (12, 3), (96, 1), (96, 2), (128, 16),
+                                         (3, 16), (64, 5)])
+def test_fold_shapes(heads, q_len):
+    log(f"fold shapes: H={heads} T={q_len}")
+    rng = np.random.default_rng(heads * 100 + q_len)
+    b = 3
+    ctx = rng.integers(q_len, 300, size=b)
+    bounds = (ctx[:, None] - (q_len - 1) + np.arange(q_len)[None, :]).astype(np.int32)
+    x = build_inputs(batch=b, heads=heads, q_len=q_len, ctx=ctx, bounds=bounds, seed=heads + q_len,
+                     latent_q=True, q_scale=1536.0)
+    d = upload(x)
+    for s in (1, 3):
+        check_latent(x, d, x.q_latent, num_splits=s, what=f"H{heads}T{q_len}S{s}")
+
+
+def test_random_bounds_zero_rows_and_empty_requests():
+    log("random bounds incl. zero rows, an all-zero request, bounds past the table")
+    rng = np.random.default_rng(5)
+    b, t, h = 5, 6, 8
+    ctx = np.array([200, 1, 0, 333, 64])
+    bounds = np.stack([rng.integers(0, c + 1, size=t) for c in ctx]).astype(np.int32)
+    bounds[2] = 0                          # a request with nothing visible
+    bounds[0, 0] = 0
+    bounds[4] = [64, 0, 64, 1, 63, 64]
+    x = build_inputs(batch=b, heads=h, q_len=t, ctx=ctx, bounds=bounds, seed=9, latent_q=True,
+                     q_scale=1536.0)
+    d = upload(x)
+    for s in (0, 1, 2, 5):
+        check_latent(x, d, x.q_latent, num_splits=s, what=f"S{s}")
+    # bounds beyond max_pages*64 are clamped to it
+    big = bounds.copy()
+    big[3, 0] = 10_000_000
+    x2 = build_inputs(batch=b, heads=h, q_len=t, ctx=ctx, bounds=np.minimum(big, 384),
+                      seed=9, latent_q=True, q_scale=1536.0)
+    d2 = upload(x2)
+    d2["kv_bounds"] = torch.from_numpy(big).cuda()
+    out, lse = mv.verify_attn(d2["q_latent"], d2["pool"], d2["block_table"], d2["kv_bounds"],
+                              x2.sm_scale, num_splits=1)
+    sync()
+    want, want_lse = oracle.verify_attention_latent(x2.q_latent, x2.pool, x2.block_table, big,
+                                                    x2.sm_scale)
+    assert_lse(lse.cpu().numpy().astype(np.float64), want_lse)
+    assert_close_output(f64_of(out), want, "clamped bounds")
+
+
+# ------------------------------------------------------------------ probes
+@pytest.mark.parametrize("splits", [1, 2, 4])
+def test_needle_probe_bit_exact(splits):
+    log(f"needle probe, S={splits}")
+    bounds = np.array([[1, 64, 65, 63], [129, 100, 128, 2], [0, 200, 255, 192],
+                       [255, 254, 253, 129]], np.int32)
+    x, pool, q, bounds = needle_case(bounds, heads=2)
+    want = needle_expected(x, bounds)
+    out, lse = mv.verify_attn(bf16_tensor(q), upload_dense_pool(pool),
+                              torch.from_numpy(x.block_table).cuda(),
+                              torch.from_numpy(bounds).cuda(), 1.0, num_splits=splits)
+    sync()
+    got = f64_of(out)
+    lse = lse.cpu().numpy()
+    for bb in range(bounds.shape[0]):
+        for t in range(bounds.shape[1]):
+            for h in range(2):
+                assert np.array_equal(got[bb, t, h], want[bb, t]), (bb, t, h, got[bb, t, h, :6])
+                assert lse[bb, t, h] == (0.0 if bounds[bb, t] > 0 else -np.inf)
+
+
+def test_page_permutation_bit_identical():
+    log("page permutation: config 2 pages moved, outputs bit-identical")
+    x = make_config(2, sharp=True)
+    q_bits = oracle_qlat_bits(x)
+    d = upload(x, q_latent_bits=q_bits)
+    _, lse1, out1 = run_latent(x, d, num_splits=4)
+    perm = np.random.default_rng(3).permutation(x.pool.num_pages)
+    x2 = make_config(2, sharp=True)
+    x2.pool = x.pool.remap(perm)
+    x2.block_table = np.where(x.block_table >= 0, perm[np.maximum(x.block_table, 0)],
+                              -1).astype(np.int32)
+    d2 = upload(x2, q_latent_bits=q_bits)
+    _, lse2, out2 = run_latent(x2, d2, num_splits=4)
+    assert np.array_equal(bits_of(out1), bits_of(out2))
+    assert np.array_equal(lse1, lse2)
+
+
+def test_deterministic_repeat():
+    log("determinism: config 3 run twice")
+    x = make_config(3, sharp=True)
+    q_bits = oracle_qlat_bits(x)
+    d = upload(x, q_latent_bits=q_bits)
+    _, l1, o1 = run_latent(x, d)
+    _, l2, o2 = run_latent(x, d)
+    assert np.array_equal(bits_of(o1), bits_of(o2)) and np.array_equal(l1, l2)
+
+
+def test_nan_pool_outside_visible_keys_is_ignored():
+    log("NaN poison: every unreferenced page and slot past the bounds is NaN")
+    x = make_config(2)
+    q_bits = oracle_qlat_bits(x)
+    d = upload(x, q_latent_bits=q_bits)
+    assert torch.isnan(d["pool"].float()).any()
+    got, lse, _ = run_latent(x, d)
+    assert np.all(np.isfinite(got)) and not np.isnan(lse).any()
+
+
+# ------------------------------------------------------------------ gated epilogue
+def check_gated(x, d, q_bits, num_splits=None, requests=None, what=""):
+    s = x.num_splits if num_splits is None else num_splits
+    out, lse, lat = mv.verify_attn_gated(d["q_latent"], d["pool"], d["block_table"],
+                                         d["kv_bounds"], d["w_uv"], d["gate"], x.sm_scale,
+                                         num_splits=s, want_latent=True)
+    sync()
+    o_lat, want_lse = oracle.verify_attention_latent(q_bits, x.pool, x.block_table, x.kv_bounds,
+                                                     x.sm_scale)
+    want = oracle.gated_output(o_lat, x.w_uv, x.gate)
+    got = f64_of(out)
+    assert_lse(lse.cpu().numpy().astype(np.float64), want_lse, f"{what} lse")
+    assert_masked_rows_zero(got, want_lse, f"{what} out")
+    assert_close_output(got, want, f"{what} gated out")
+    assert_close_output(f64_of(lat), o_lat, f"{what} gated out_latent")
+
+
+@pytest.mark.parametrize("cfg,splits", [(1, 1), (1, 2), (3, 4), (5, 8)])
+def test_gated_parity(cfg, splits):
+    log(f"gated parity: config {cfg}, S={splits}")
+    x = make_config(cfg, sharp=(cfg != 5))
+    q_bits = oracle_qlat_bits(x)
+    d = upload(x, q_latent_bits=q_bits)
+    check_gated(x, d, q_bits, num_splits=splits, what=f"cfg{cfg}")
+
+
+# ------------------------------------------------------------------ end to end
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_end_to_end_against_unabsorbed_oracle(cfg):
+    """HIP absorption + HIP attention (+ gated epilogue) against the oracle's
+    primary, unabsorbed definition (explicit per-head K/V up-projection)."""
+    log(f"end to end vs unabsorbed oracle: config {cfg}")
+    x = make_config(cfg)
+    d = upload(x)
+    q_lat = mv.verify_absorb_q(d["q_nope"], d["w_uk"])
+    out_lat, lse = mv.verify_attn(q_lat, d["pool"], d["block_table"], d["kv_bounds"], x.sm_scale)
+    out, lse_g, _ = mv.verify_attn_gated(q_lat, d["pool"], d["block_table"], d["kv_bounds"],
+                                         d["w_uv"], d["gate"], x.sm_scale)
+    sync()
+    r = oracle.verify_attention_mla(x.q_nope, x.w_uk, x.w_uv, x.gate, x.pool, x.block_table,
+                                    x.kv_bounds, x.sm_scale)
+    assert_lse(lse.cpu().numpy().astype(np.float64), r["lse"])
+    assert_lse(lse_g.cpu().numpy().astype(np.float64), r["lse"])
+    assert_close_output(f64_of(out_lat), r["o_lat"], "o_lat")
+    assert_close_output(f64_of(out), r["out"], "gated out")
+    assert rel_l2(f64_of(out), r["out"]) < 5e-3
+
+
+def test_fp8_request_raises():
+    log("fp8 KV request is rejected")
+    x = make_config(1)
+    d = upload(x, q_latent_bits=oracle_qlat_bits(x))
+    with pytest.raises(mv.MlaVerifyError, match="MLA_ERR_DTYPE"):
+        mv.verify_attn(d["q_latent"], d["pool"], d["block_table"], d["kv_bounds"], x.sm_scale,
+                       kv_dtype=mv.KV_FP8_E4M3)
