@@ -115,9 +115,9 @@ int mla_verify_check(const mla_verify_params* p);
 int mla_verify_num_splits(const mla_verify_params* p, int gated);
 
 /* Workspace bytes the call needs (0 when it needs none).  `gated` selects
- * mla_verify_attn_gated.  Pure host code.  Layout (fp32): partial outputs
- * [S][B*T*H][512] then partial LSEs [S][B*T*H].  Returns MLA_OK or an
- * error code; *bytes is written only on success. */
+ * mla_verify_attn_gated.  Pure host code.  Layout: normalised partial
+ * outputs [S][B*T*H][512] in bf16, then partial LSEs [S][B*T*H] in fp32.
+ * Returns MLA_OK or an error code; *bytes is written only on success. */
 int mla_verify_workspace_size(const mla_verify_params* p, int gated, size_t* bytes);
 
 /* Verify attention, latent output.

@@ -32,15 +32,26 @@ int check_params(const mla_verify_params* p) {
   return MLA_OK;
 }
 
+TileShape choose_shape(int rows) {
+  // Up to 64 rows: one tile holds every row of a request, so each page is
+  // staged once per split; the four waves split its keys in QK.  More rows:
+  // tiles of 128 rows (each wave owns 32 rows in QK), which keeps the number
+  // of times a page is re-staged per request small.
+  if (rows <= 32) return TileShape{0};
+  if (rows <= 64) return TileShape{1};
+  return TileShape{2};
+}
+
 Plan make_plan(const mla_verify_params* p, bool gated) {
   Plan pl{};
   pl.rows = p->q_len * p->num_heads;
-  pl.row_tiles = (pl.rows + kTileRows - 1) / kTileRows;
+  pl.shape = choose_shape(pl.rows);
+  pl.row_tiles = (pl.rows + pl.shape.tile_rows() - 1) / pl.shape.tile_rows();
   int s = p->num_splits;
   if (s == 0) {
     // Library's choice: about one workgroup per compute unit (a workgroup
-    // holds ~138 KiB of LDS, so one fits per CU), and at least two pages per
-    // split, since every split writes an fp32 partial row tile.
+    // holds ~150 KiB of LDS, so one fits per CU), and at least two pages per
+    // split, since every split writes a partial row tile.
     const int64_t tiles = (int64_t)p->batch * pl.row_tiles;
     int64_t want = (kNumCUs + tiles / 2) / tiles;
     const int64_t cap = p->max_pages_per_req / 2 > 1 ? p->max_pages_per_req / 2 : 1;
@@ -54,8 +65,9 @@ Plan make_plan(const mla_verify_params* p, bool gated) {
   pl.splits = s;
   pl.use_partials = gated || s > 1;
   const size_t total_rows = (size_t)p->batch * pl.rows;
+  // partial outputs in bf16, partial LSEs in fp32
   pl.workspace_bytes =
-      pl.use_partials ? (size_t)s * total_rows * (MLA_VERIFY_LATENT + 1) * sizeof(float) : 0;
+      pl.use_partials ? (size_t)s * total_rows * (MLA_VERIFY_LATENT * 2 + sizeof(float)) : 0;
   return pl;
 }
 

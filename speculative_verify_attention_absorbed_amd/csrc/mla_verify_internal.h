@@ -9,19 +9,30 @@
 
 namespace mla {
 
-constexpr int kTileRows = 32;   // folded rows per attention workgroup
-constexpr int kNumCUs = 256;    // MI355X compute units
-constexpr int kNumXCDs = 8;     // dies; workgroups are dealt to them round-robin
+constexpr int kNumCUs = 256;           // MI355X compute units
+constexpr int kNumXCDs = 8;            // dies; workgroups are dealt to them round-robin
 constexpr int kMaxSplitPages = 1024;   // block-table entries one split stages in LDS
+
+// Shape of one attention workgroup (always four wavefronts).
+//   mode 0: 32-row tile, 64-key staging units, QK split by keys
+//   mode 1: 64-row tile, 64-key staging units, QK split by keys
+//   mode 2: 128-row tile, 32-key staging units, QK split by rows
+// PV always splits the 512 latent dims between the four waves.
+struct TileShape {
+  int mode;
+  int tile_rows() const { return mode == 0 ? 32 : (mode == 1 ? 64 : 128); }
+};
 
 struct Plan {
   int rows;             // R = T * H folded rows per request
-  int row_tiles;        // ceil(R / kTileRows)
+  TileShape shape;
+  int row_tiles;        // ceil(R / tile rows)
   int splits;           // S
-  bool use_partials;    // results go through the fp32 partial workspace
+  bool use_partials;    // results go through the partial workspace (bf16 O, fp32 LSE)
   size_t workspace_bytes;
 };
 
+TileShape choose_shape(int rows);
 int check_params(const mla_verify_params* p);
 Plan make_plan(const mla_verify_params* p, bool gated);
 bool aligned16(const void* ptr);

@@ -76,61 +76,171 @@ struct AttnArgs {
   const int32_t* bounds;   // [B, T]
   uint16_t* out_lat;       // [B, R, 512] (direct mode)
   float* lse;              // [B, R]      (direct mode)
-  float* part_o;           // [S, B*R, 512] (split mode)
+  uint16_t* part_o;        // [S, B*R, 512] bf16 (split mode)
   float* part_lse;         // [S, B*R]
   int B, T, H, R, P, N, S, row_tiles;
   float scale_log2;        // sm_scale * log2(e)
   int direct;              // 1: write out_lat/lse, 0: write partials
 };
 
-constexpr int kRows = mla::kTileRows;          // 32 folded rows per workgroup
-// A key row of the LDS page tile is 1024 bytes of latent plus 32 bytes of
-// padding: the four key rows one transposing read touches then fall on four
-// disjoint 8-bank groups, and every access is one base register plus an
-// immediate offset.
-constexpr int kRowChunks = D / 8 + 2;          // 66 16-byte chunks per key row
-constexpr int kPageChunks = PG * kRowChunks;   // 4224 chunks (67584 bytes) per page
-constexpr int kPStride = PG + 8;               // bf16 per P row (padded: fewer bank conflicts)
-constexpr int kMaxSplitPages = mla::kMaxSplitPages;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+typedef __attribute__((ext_vector_type(8))) short s16x8;
 
-struct AttnSmem {
-  uint4 page[2][kPageChunks];          // double-buffered latent page (padded key rows)
-  uint16_t p[2][kRows * kPStride];     // P (bf16), [row][key]
-  float wmax[2][4][kRows];             // per-wave row maxima of the page
-  float lsum[2][4][kRows];             // per-wave denominators: [0] bf16-rounded P, [1] exact
-  int32_t pages[kMaxSplitPages];       // this split's block-table slice
-};
+constexpr int kBufBytes = 128 * 1024;                           // key-row staging buffers
+constexpr int kPBytes = 10 * 1024;                              // P tile (bf16, padded rows)
+constexpr int kStatFloats = 13 * 128;                           // per-row maxima, reference, sums
+constexpr int kAttnSmemBytes =
+    kBufBytes + kPBytes + mla::kMaxSplitPages * 4 + kStatFloats * 4 + 16;
+// Softmax reference without rescaling: a row's reference max is fixed by the
+// first unit in which it sees a key (O and the sums are still exactly zero
+// then), and P = 2^(s - ref) may exceed 1 afterwards.  While no score exceeds
+// the reference by more than kMaxJump (log2 domain) nothing can overflow
+// (P <= 2^64, |O| <= 2^64 * |V| * keys); a row that jumps further makes the
+// workgroup run its item a second time with every reference preset to the
+// true maximum, where P <= 1.  The O tile is never touched by vector ALU
+// instructions inside the key loop, which keeps it in accumulation registers.
+constexpr float kMaxJump = 64.f;
+
+// XOR swizzle of the 16-byte chunk index of a key row in LDS, a function of
+// the key's low four bits.  With it, the 16 keys one K-operand read touches
+// at one chunk, and the 4 (or 8) keys one transposing V read touches at one
+// 32-byte pair, fall on distinct banks, for 128- and 256-byte LDS rows alike.
+__device__ __forceinline__ int swz16(int k) {
+  const int q = (k >> 2) & 3;
+  return ((k & 3) << 1) | ((q & 1) ^ (q >> 1)) | ((q & 1) << 3);
+}
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// One 1 KiB key row HBM -> LDS without passing through registers: lane l
+// fetches the 16 bytes at base + voff and the hardware writes them to LDS
+// byte address lds + 16 l.  Written as inline assembly so that the compiler,
+// which cannot tell the staging buffers apart, does not drain every
+// outstanding load before each LDS read; the kernel waits explicitly.
+__device__ __forceinline__ void dma_row16(const void* base, uint32_t voff, uint32_t lds) {
+  // base and lds are the same for every lane; make that explicit (SGPR operands)
+  const uint64_t bp = reinterpret_cast<uint64_t>(base);
+  const uint64_t bu = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(bp >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)bp);
+  base = reinterpret_cast<const void*>(bu);
+  lds = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               ::"v"(voff), "s"(base), "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// O^T += V^T P^T for one 16x16 block, written so the accumulator is pinned to
+// the accumulation registers (the 32-row O tile fills all 256 of them, and
+// the compiler's register assignment otherwise shuttles it to and from
+// VGPRs).  Inline assembly is invisible to the compiler's hazard tracking, so
+// the instruction carries its own wait: a VALU write of an MFMA source needs
+// two wait states; the other direction (MFMA result read by VALU) is covered
+// by settle_acc().
+__device__ __forceinline__ void mfma16_acc(f32x4& acc, const bf16x8& a_op, const bf16x8& b_op) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
+               : "+a"(acc) : "v"(a_op), "v"(b_op));
+}
+// S^T += K Q^T for one 16x16 block, accumulator pinned to VGPRs (the
+// accumulation registers hold the O tile).  Same two-wait-state guard.
+__device__ __forceinline__ void mfma16_vacc(f32x4& acc, const bf16x8& a_op, const bf16x8& b_op) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
+               : "+v"(acc) : "v"(a_op), "v"(b_op));
+}
+// Same, with the B operand (a Q^T block) held in accumulation registers: a
+// 64-row Q^T tile does not fit in VGPRs next to everything else.
+__device__ __forceinline__ void mfma16_vacc_aq(f32x4& acc, const bf16x8& a_op, const bf16x8& b_op) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
+               : "+v"(acc) : "v"(a_op), "a"(b_op));
+}
+// Wait states between the last MFMAs writing `acc` and a VALU access of it:
+// callers settle the accumulators of the last 8 PV MFMAs in write order, so
+// with the 3 issue slots of every later MFMA each is at least 24 wait states
+// past its last write.
+__device__ __forceinline__ void settle_acc(f32x4& acc) { asm volatile("s_nop 7" : "+a"(acc)); }
+
+// Wait until at most `allowed` of this wave's vector-memory operations are
+// outstanding and its LDS writes are done, then barrier.  Memory operations
+// complete in issue order, so rounding `allowed` down is always safe.
+__device__ __forceinline__ void wait_vm_barrier(int allowed) {
+  if (allowed >= 32)
+    asm volatile("s_waitcnt vmcnt(32) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if (allowed >= 16)
+    asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if (allowed >= 8)
+    asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 // Logical work item of a workgroup.  Hardware deals workgroups to the 8 XCDs
 // round-robin (bid % 8); logical items are laid out in contiguous runs per
-// XCD, so the row tiles that read the same pages share one L2.  Returns -1
-// for the padding workgroups of a grid rounded up to a multiple of 8.
+// XCD, so the row tiles and splits that read the same pages share one L2.
+// Returns -1 for the padding workgroups of a grid rounded up to a multiple of 8.
 __device__ __forceinline__ int logical_item(int bid, int n_items) {
   const int per = (n_items + mla::kNumXCDs - 1) / mla::kNumXCDs;
   const int li = (bid % mla::kNumXCDs) * per + bid / mla::kNumXCDs;
   return li < n_items ? li : -1;
 }
 
-typedef uint4 KStage[16];
+// Verify attention over one (request b, KV split s, row tile) work item.
+// Four wavefronts; MODE picks the tile:
+//   MODE 0 / 1   a tile of 32 / 64 folded rows (every row of a request with
+//                R <= 64), 64-key staging units.  QK splits the unit's keys
+//                between the waves (wave w: keys 16w .. +15, all rows), so
+//                every latent byte is read from LDS once by the QK reads.
+//   MODE 2       a tile of 128 rows, 32-key units.  QK splits the rows (wave
+//                w: rows 32w .. +31, all 32 keys).
+// In both, PV splits the latent dims (wave w: dims 128w .. +127, all rows):
+//   S = Q K^T   bf16 MFMA 16x16x32, K from LDS (ds_read_b128), Q^T in
+//               registers for the whole item; masked by each row's own
+//               bound; P = 2^(s - ref) in bf16 goes to a small LDS tile
+//   O += P V    bf16 MFMA 16x16x32, V^T from LDS (ds_read_b64_tr_b16), P^T
+//               from the tile; every O element lives in exactly one wave.
+// Softmax without rescaling: every row with a visible key in this split sees
+// one in unit 0 (the split's first key is visible whenever any is), so each
+// row's reference max is fixed there for the whole item; P may exceed 1
+// later (see kMaxJump for the second pass).
+template <int MODE>
+__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
+  constexpr bool KS = MODE < 2;                 // key-split QK
+  constexpr int NRB = MODE == 0 ? 2 : (MODE == 1 ? 4 : 8);   // 16-row blocks of the tile
+  constexpr int RT = 16 * NRB;                  // rows per tile
+  constexpr int UK = KS ? 64 : 32;              // keys per staging unit
+  constexpr int NBUF = kBufBytes / (UK * 1024); // units the buffers hold
+  constexpr int ROWS_PW = UK / 4;               // key rows each wave stages per unit
+  constexpr int QKB = KS ? 1 : 2;               // 16-key blocks per wave in QK
+  constexpr int QRB = KS ? NRB : 2;             // 16-row blocks per wave in QK
+  constexpr int KK = UK / 32;                   // 32-key MFMA steps per unit in PV
+  constexpr int NDT = 8;                        // 16-dim blocks of O per wave
+  constexpr int PPITCH = UK * 2 + 16;           // bytes per P row (padding spreads banks)
+  constexpr int NSLOT = KS ? 4 : 1;             // waves contributing to one row's sums
+  static_assert(RT * PPITCH <= kPBytes, "P tile");
 
-// Workgroup = 4 waves over one (request b, KV split s, 32-row tile).
-//  QK^T: wave w owns keys 16w..16w+15 of every page and all 32 rows; its K
-//        operand is loaded straight from HBM into registers (the MFMA A
-//        layout is the cache's own row-major layout), Q^T (32 rows) stays in
-//        registers.  Two register stages keep two pages in flight.  The same
-//        registers are written to LDS once, where the page serves as V.
-//  softmax: per-wave row maxima are exchanged through LDS; every wave then
-//        derives the same running max, so rescale factors agree across waves.
-//  PV:   wave w owns latent dims 128w..128w+127 for all 32 rows; V^T comes
-//        from LDS through ds_read_tr16_b64, P^T through a small LDS buffer.
-__global__ __launch_bounds__(kThreads) void verify_attn_kernel(AttnArgs a) {
-  extern __shared__ uint4 smem_raw[];
-  AttnSmem& sm = *reinterpret_cast<AttnSmem*>(smem_raw);
+  extern __shared__ uint4 smem[];
+  lds_u8* sb = (lds_u8*)smem;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)sb;
+  lds_u8* sp = sb + kBufBytes;                   // P tile
+  __attribute__((address_space(3))) int32_t* sm_pid =
+      (__attribute__((address_space(3))) int32_t*)(sb + kBufBytes + kPBytes);
+  lds_f32* sst = (lds_f32*)(sb + kBufBytes + kPBytes + mla::kMaxSplitPages * 4);
+  lds_f32* xm = sst;                             // [4][RT] per-wave row maxima
+  lds_f32* st_m = sst + 4 * RT;                  // [RT] reference per row
+  lds_f32* st_lr = sst + 5 * RT;                 // [NSLOT][RT]
+  lds_f32* st_le = sst + (5 + NSLOT) * RT;       // [NSLOT][RT]
+  __attribute__((address_space(3))) int32_t* sm_redo =
+      (__attribute__((address_space(3))) int32_t*)(sst + kStatFloats);
+
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int g = lane >> 4;
-  const int i16 = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
+  const int g = lane >> 4, i16 = lane & 15;
 
   int id = logical_item(blockIdx.x, a.B * a.S * a.row_tiles);
   if (id < 0) return;
@@ -139,227 +249,452 @@ __global__ __launch_bounds__(kThreads) void verify_attn_kernel(AttnArgs a) {
   const int s = id % a.S;
   const int b = id / a.S;
 
-  const int row0 = rt * kRows;
-  const int rows_here = min(kRows, a.R - row0);
+  const int row0 = rt * RT;
+  const int rows_here = min(RT, a.R - row0);
   const int max_keys = a.P * PG;
+  // tile row of this lane's QK row block rb, and the first key of QK key block kb
+  auto qrow = [&](int rb) { return (KS ? 0 : 32 * w) + 16 * rb + i16; };
+  auto qkey = [&](int kb) { return KS ? 16 * w : 16 * kb; };
 
-  // ---- independent loads first: row bounds, tile bounds, Q
-  int L[2];
-  bool rvalid[2];
+  // ---- bounds of the tile's tokens (lane j: token t_lo + j; at most 16)
+  const int t_lo = row0 / a.H;
+  const int ntok = (row0 + rows_here - 1) / a.H - t_lo + 1;
+  const int tb = (lane < ntok) ? clampi(a.bounds[b * a.T + t_lo + lane], 0, max_keys) : 0;
+
+  // ---- Q^T of this wave's QK rows.  Row-split tiles load their own rows
+  // here (in flight while the first pages stream); key-split tiles, where
+  // every wave needs every row, stage the tile once through LDS below.
+  bf16x8 qreg[QRB][16];   // qreg[rb][ks] = Q[tile row qrow(rb)][32 ks + 8 g .. +7]
+  if constexpr (!KS) {
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int r = row0 + nt * 16 + i16;
-    rvalid[nt] = r < a.R;
-    L[nt] = rvalid[nt] ? clampi(a.bounds[b * a.T + r / a.H], 0, max_keys) : 0;
-  }
-  bf16x8 qreg[2][16];   // Q^T operand: qreg[nt][ks] = q[row r_nt][ks*32 + 8g .. +7]
+    for (int rb = 0; rb < QRB; ++rb) {
+      const int r = min(row0 + qrow(rb), a.R - 1);
+      const uint4* qp = reinterpret_cast<const uint4*>(a.q + ((size_t)b * a.R + r) * D);
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int r = rvalid[nt] ? row0 + nt * 16 + i16 : 0;
-    const uint4* qrow = reinterpret_cast<const uint4*>(a.q + ((size_t)b * a.R + r) * D);
+      for (int ks = 0; ks < 16; ++ks) qreg[rb][ks] = __builtin_bit_cast(bf16x8, qp[ks * 4 + g]);
+    }
+  }
+
+  int n_tile = tb;
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) qreg[nt][ks] = __builtin_bit_cast(bf16x8, qrow[ks * 4 + g]);
+  for (int off = 32; off >= 1; off >>= 1) n_tile = max(n_tile, __shfl_xor(n_tile, off));
+  n_tile = __builtin_amdgcn_readfirstlane(n_tile);
+  int L[QRB];           // bounds of this lane's QK rows
+  int lmin = INT_MAX;   // smallest bound among the wave's valid QK rows
+#pragma unroll
+  for (int rb = 0; rb < QRB; ++rb) {
+    const int r = row0 + qrow(rb);
+    const int lr = __shfl(tb, min(r, a.R - 1) / a.H - t_lo);
+    L[rb] = r < a.R ? lr : 0;
+    if (r < a.R) lmin = min(lmin, lr);
   }
-  int n_tile = 0;   // keys the tile scans: the largest bound among its tokens
-  {
-    const int t_lo = row0 / a.H;
-    const int t_hi = (row0 + rows_here - 1) / a.H;
-    for (int t = t_lo; t <= t_hi; ++t) n_tile = max(n_tile, clampi(a.bounds[b * a.T + t], 0, max_keys));
-  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) lmin = min(lmin, __shfl_xor(lmin, off));
+  lmin = __builtin_amdgcn_readfirstlane(lmin);
+
   const int n_pg = (n_tile + PG - 1) / PG;
   const int p_begin = (s * n_pg) / a.S;
-  const int n_my = ((s + 1) * n_pg) / a.S - p_begin;   // <= ceil(P / S) <= kMaxSplitPages
+  const int p_end = ((s + 1) * n_pg) / a.S;   // p_end - p_begin <= kMaxSplitPages (host check)
+  const int k_begin = p_begin * PG;
+  const int k_end = min(p_end * PG, n_tile);
+  const int n_units = k_end > k_begin ? (k_end - k_begin + UK - 1) / UK : 0;
 
-  // ---- stage this split's page ids in LDS
-  for (int i = tid; i < n_my; i += kThreads) sm.pages[i] = a.bt[b * a.P + p_begin + i];
-  __syncthreads();
+  for (int i = tid; i < p_end - p_begin; i += 256) sm_pid[i] = a.bt[b * a.P + p_begin + i];
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-  const int my_key = 16 * w + i16;
-  // K operand of page j (0-based within the split): kst[ks] = key my_key,
-  // dims ks*32 + 8g .. +7.  Slots past n_tile and bad page ids read as zero.
-  auto load_page = [&](KStage& kst, int j) {
-    const int pid = sm.pages[j];
-    const bool ok = (unsigned)pid < (unsigned)a.N && ((p_begin + j) * PG + my_key) < n_tile;
-    const uint4* src = reinterpret_cast<const uint4*>(a.pool + ((size_t)(ok ? pid : 0) * PG + my_key) * D);
+  // Stage unit u into buffer u % NBUF.  Key rows past the tile's extent, and
+  // rows of a page whose id is out of range, are zero-filled instead (never
+  // read from the pool), so 0 * garbage never reaches the PV contraction.
+  auto issue_unit = [&](int u) {
+    const uint32_t ub = (uint32_t)(u % NBUF) * (UK * 1024);
+    const int kl = u * UK;                         // key offset within the split
+    const int pid = __builtin_amdgcn_readfirstlane(sm_pid[kl >> 6]);
+    const bool pid_ok = (unsigned)pid < (unsigned)a.N;
+    const uint16_t* pbase = a.pool + ((size_t)(pid_ok ? pid : 0) * PG + (kl & 63)) * D;
+#pragma unroll 8
+    for (int i = 0; i < ROWS_PW; ++i) {
+      const int kap = w + 4 * i;                   // key row within the unit
+      if (pid_ok && k_begin + kl + kap < n_tile) {
+        dma_row16(pbase + kap * D, 16u * (uint32_t)(lane ^ swz16(kap & 15)),
+                  lds0 + ub + (uint32_t)kap * 1024u);
+      } else {
+        *(lds_u32x4*)(sb + ub + kap * 1024 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  // DMA instructions this wave issued for unit u (rows skipped above issue none)
+  auto unit_ops = [&](int u) {
+    if (u >= n_units) return 0;
+    const int kl = u * UK;
+    const int pid = __builtin_amdgcn_readfirstlane(sm_pid[kl >> 6]);
+    if ((unsigned)pid >= (unsigned)a.N) return 0;
+    const int valid = n_tile - (k_begin + kl);      // rows of the unit below n_tile
+    if (valid >= UK) return ROWS_PW;
+    int c = 0;
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-      const uint4 v = src[ks * 4 + g];
-      kst[ks] = ok ? v : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < ROWS_PW; ++i) c += (w + 4 * i) < valid;
+    return c;
+  };
+
+  // LDS byte offsets (within a unit buffer) of this lane's operand reads.
+  // K rows qkey(kb) + i16, chunk 4 ks + g: qkb[ks & 3] + 64 (ks & 12) + 1024 qkey(kb)
+  const int swl = swz16(i16);
+  uint32_t qkb[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    qkb[j] = (uint32_t)(i16 * 1024 + 64 * (j ^ (swl >> 2)) + 16 * (g ^ (swl & 3)));
+  // V^T: lanes 4q..4q+3 of lane group g address key rows 8g + q (+4 for the
+  // second read; +32 kk for k-step kk) at dims 16 D16 + 4 (i16 & 3).  For a
+  // dim block D16: offset = trb[hi][D16 & 7] + 256 (D16 >> 3) + 32768 kk.
+  uint32_t trb[2][8];
+  {
+    const int q = i16 >> 2, e4 = i16 & 3;
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int k32 = 8 * g + q + 4 * hi;
+      const int sv = swz16(k32 & 15);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        trb[hi][j] = (uint32_t)(k32 * 1024 + 32 * (j ^ (sv >> 1)) + 16 * ((e4 >> 1) ^ (sv & 1)) +
+                                8 * (e4 & 1));
+    }
+  }
+  // P tile: this lane writes rows qrow(rb), keys qkey(kb) + 4g .. +3 and reads
+  // the PV B operand P[row 16 rb + i16][32 kk + 8 g .. +7]
+  const uint32_t pr_off = (uint32_t)(i16 * PPITCH + 16 * g);
+
+  f32x4 o[NDT][NRB];   // O^T: o[dt][rb][i] = O[row 16 rb + i16][dim 128 w + 16 dt + 4 g + i]
+  float mref[QRB];     // reference max of this lane's QK rows (log2 domain)
+  float mtrue[QRB];    // lane's running max of its own scores
+  float lround[QRB];   // lane share of sum of bf16(P): the weights PV applies
+  float lexact[QRB];   // lane share of sum of P in fp32: the LSE
+  float mpreset[QRB];
+  bool jumped = false;
+#pragma unroll
+  for (int rb = 0; rb < QRB; ++rb) mpreset[rb] = -INFINITY;
+
+  // row max over the 4 lane groups; for key-split tiles also over the 4 waves
+  auto row_reduce_max = [&](float (&m)[QRB]) {
+#pragma unroll
+    for (int rb = 0; rb < QRB; ++rb) {
+      m[rb] = fmaxf(m[rb], __shfl_xor(m[rb], 16));
+      m[rb] = fmaxf(m[rb], __shfl_xor(m[rb], 32));
+    }
+    if constexpr (KS) {
+      if (g == 0) {
+#pragma unroll
+        for (int rb = 0; rb < QRB; ++rb) xm[w * RT + qrow(rb)] = m[rb];
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+      for (int rb = 0; rb < QRB; ++rb)
+        m[rb] = fmaxf(fmaxf(xm[qrow(rb)], xm[RT + qrow(rb)]), fmaxf(xm[2 * RT + qrow(rb)], xm[3 * RT + qrow(rb)]));
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // xm free again
     }
   };
 
-  f32x4 o[8][2];   // O^T: o[dt][nt][i] = O[row r_nt][dim 128w + 16dt + 4g + i]
+  auto compute_unit = [&](int u, int pass) {
+    const uint32_t ub = (uint32_t)(u % NBUF) * (UK * 1024);
+    const int ukey0 = k_begin + u * UK;            // request position of the unit's first key
+    // ---- S^T = K Q^T: sacc[kb][rb][i] = score(key qkey(kb) + 4g + i, row qrow(rb))
+    f32x4 sacc[QKB][QRB];
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt)
+    for (int kb = 0; kb < QKB; ++kb)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) o[dt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m[2] = {-INFINITY, -INFINITY};   // running row max (log2 domain), same in every wave
-  // this lane's share of the denominator: lround sums the bf16-rounded P that
-  // feeds PV (so the output weights sum to one), lexact the fp32 values (LSE)
-  float lround[2] = {0.f, 0.f};
-  float lexact[2] = {0.f, 0.f};
-
-  KStage kA, kB;
-  if (n_my > 0) load_page(kA, 0);
-  if (n_my > 1) load_page(kB, 1);
-
-  auto process = [&](KStage& kst, int j) {
-    const int buf = j & 1;
-    const int p = p_begin + j;
-    // ---- S^T = K Q^T: sacc[nt][i] = score(key 16w + 4g + i, row r_nt)
-    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      for (int rb = 0; rb < QRB; ++rb) sacc[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    constexpr int KPG = 4 / QKB;   // k-steps per operand group (4 reads per group)
+    bf16x8 kop[2][KPG][QKB];
+    auto load_k = [&](bf16x8 (&dst)[KPG][QKB], int grp) {
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-      const bf16x8 kv = __builtin_bit_cast(bf16x8, kst[ks]);
-      sacc[0] = mfma16(kv, qreg[0][ks], sacc[0]);
-      sacc[1] = mfma16(kv, qreg[1][ks], sacc[1]);
-    }
-    // ---- the page's keys go to LDS, where they serve as V; then the stage
-    // is refilled with page j+2
+      for (int e = 0; e < KPG; ++e) {
+        const int ks = KPG * grp + e;
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) sm.page[buf][my_key * kRowChunks + ks * 4 + g] = kst[ks];
-
-    // ---- mask + per-wave row maxima
-    const int kpos0 = p * PG + 16 * w + 4 * g;
-    float sv[2][4];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float v = (kpos0 + i) < L[nt] ? sacc[nt][i] * a.scale_log2 : -INFINITY;
-        sv[nt][i] = v;
-        mx = fmaxf(mx, v);
+        for (int kb = 0; kb < QKB; ++kb)
+          dst[e][kb] = *(const lds_bf16x8*)(sb + ub + qkb[ks & 3] + 64 * (ks & 12) + 1024 * qkey(kb));
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      if (g == 0) sm.wmax[buf][w][nt * 16 + i16] = mx;
-    }
-    __syncthreads();   // (A) maxima and the V page are visible
-
-    float alpha[2];
+    };
+    constexpr int NGRP = 16 / KPG;
+    load_k(kop[0], 0);
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int r = nt * 16 + i16;
-      const float pm = fmaxf(fmaxf(sm.wmax[buf][0][r], sm.wmax[buf][1][r]),
-                             fmaxf(sm.wmax[buf][2][r], sm.wmax[buf][3][r]));
-      const float m_new = fmaxf(m[nt], pm);
-      const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;   // nothing visible yet: p = 0
-      alpha[nt] = exp2f(m[nt] - m_ref);
-      m[nt] = m_new;
-      uint32_t pb[4];
-      float ps = 0.f, pe = 0.f;
+    for (int grp = 0; grp < NGRP; ++grp) {
+      if (grp + 1 < NGRP) load_k(kop[(grp + 1) & 1], grp + 1);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pv = exp2f(sv[nt][i] - m_ref);
-        pb[i] = bf16_rne(pv);
-        ps += bf16_to_f32(pb[i]);
-        pe += pv;
+      for (int e = 0; e < KPG; ++e) {
+        const int ks = KPG * grp + e;
+#pragma unroll
+        for (int kb = 0; kb < QKB; ++kb)
+#pragma unroll
+          for (int rb = 0; rb < QRB; ++rb) {
+            if (rb < 2) mfma16_vacc(sacc[kb][rb], kop[grp & 1][e][kb], qreg[rb][ks]);
+            else mfma16_vacc_aq(sacc[kb][rb], kop[grp & 1][e][kb], qreg[rb][ks]);
+          }
       }
-      lround[nt] = lround[nt] * alpha[nt] + ps;
-      lexact[nt] = lexact[nt] * alpha[nt] + pe;
-      uint2 pw;
-      pw.x = pb[0] | (pb[1] << 16);
-      pw.y = pb[2] | (pb[3] << 16);
-      *reinterpret_cast<uint2*>(&sm.p[buf][r * kPStride + 16 * w + 4 * g]) = pw;
+      __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      o[dt][0] *= alpha[0];
-      o[dt][1] *= alpha[1];
+    // MFMA result -> VALU read: at least 11 wait states, ordered after the last
+    // MFMA writing any of the score blocks
+    static_assert(QKB * QRB == 2 || QKB * QRB == 4, "score blocks per wave");
+    {
+      f32x4* sf = &sacc[0][0];
+      if constexpr (QKB * QRB == 4)
+        asm volatile("s_nop 7\n\ts_nop 4" : "+v"(sf[0]), "+v"(sf[1]), "+v"(sf[2]), "+v"(sf[3]));
+      else
+        asm volatile("s_nop 7\n\ts_nop 4" : "+v"(sf[0]), "+v"(sf[1]));
     }
-    __syncthreads();   // (B) P is visible
-
-    // ---- O^T += V^T P^T over the page's 64 keys.  k-slots of step kk are
-    // keys 32kk + 8g + (0..7) for both operands.
-    const lds_s16x4* vpage = (const lds_s16x4*)(&sm.page[buf][0]);
+    // ---- masked scores in the log2 domain
+    float sv[QKB][QRB][4];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      bf16x8 pop[2];
+    for (int kb = 0; kb < QKB; ++kb) {
+      const int key = ukey0 + qkey(kb) + 4 * g;
+      const bool full = key + 4 <= lmin;   // every valid row sees these 4 keys
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-        pop[nt] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const uint4*>(&sm.p[buf][(nt * 16 + i16) * kPStride + 32 * kk + 8 * g]));
-      // transposing read: lanes 4r..4r+3 of a 16-lane group address key row
-      // kb + r (4 dims each); lane j receives dim j of those 4 rows.
-      // (in 8-byte units: a key row is 2*kRowChunks units, 4 dims per unit)
-      const int kb = 32 * kk + 8 * g + (i16 >> 2);
-      const lds_s16x4* vrow = vpage + kb * (2 * kRowChunks) + 32 * w + (i16 & 3);
+      for (int rb = 0; rb < QRB; ++rb)
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            const_cast<lds_s16x4*>(vrow + 4 * dt));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            const_cast<lds_s16x4*>(vrow + 4 * (2 * kRowChunks) + 4 * dt));
-        uint4 av;
-        av.x = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
-        av.y = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
-        av.z = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
-        av.w = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
-        const bf16x8 vop = __builtin_bit_cast(bf16x8, av);
-        o[dt][0] = mfma16(vop, pop[0], o[dt][0]);
-        o[dt][1] = mfma16(vop, pop[1], o[dt][1]);
+        for (int i = 0; i < 4; ++i) {
+          float v = sacc[kb][rb][i] * a.scale_log2;
+          if (!full) v = (key + i) < L[rb] ? v : -INFINITY;
+          sv[kb][rb][i] = v;
+        }
+    }
+    if (u == 0) {   // fix every row's reference for the whole item
+      if (pass == 0) {
+        float m[QRB];
+#pragma unroll
+        for (int rb = 0; rb < QRB; ++rb) {
+          m[rb] = -INFINITY;
+#pragma unroll
+          for (int kb = 0; kb < QKB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) m[rb] = fmaxf(m[rb], sv[kb][rb][i]);
+        }
+        row_reduce_max(m);
+#pragma unroll
+        for (int rb = 0; rb < QRB; ++rb) mref[rb] = m[rb];
+      } else {
+#pragma unroll
+        for (int rb = 0; rb < QRB; ++rb) mref[rb] = mpreset[rb];
       }
     }
-    if (j + 2 < n_my) load_page(kst, j + 2);   // refill this stage with page j+2
+    // ---- P = 2^(s - ref) in bf16 into the P tile; lane sums and maxima
+#pragma unroll
+    for (int rb = 0; rb < QRB; ++rb) {
+      const float mu = (mref[rb] == -INFINITY) ? 0.f : mref[rb];   // no visible key: P = 0
+      float sr = 0.f, se = 0.f, mt = mtrue[rb];
+#pragma unroll
+      for (int kb = 0; kb < QKB; ++kb) {
+        __bf16 pv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          mt = fmaxf(mt, sv[kb][rb][i]);
+          const float p = __builtin_amdgcn_exp2f(sv[kb][rb][i] - mu);   // v_exp_f32; -inf -> 0
+          pv[i] = (__bf16)p;
+          sr += (float)pv[i];
+          se += p;
+        }
+        const u32x2 pw = {
+            (uint32_t)__builtin_bit_cast(uint16_t, pv[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, pv[1]) << 16),
+            (uint32_t)__builtin_bit_cast(uint16_t, pv[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, pv[3]) << 16)};
+        *(lds_u32x2*)(sp + qrow(rb) * PPITCH + 2 * (qkey(kb) + 4 * g)) = pw;
+      }
+      mtrue[rb] = mt;
+      jumped |= mt > mref[rb] + kMaxJump;
+      lround[rb] += sr;
+      lexact[rb] += se;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // P tile complete
+    // ---- O^T += V^T P^T over this wave's latent dims and all RT rows
+    bf16x8 pop[NRB][KK];   // P[row 16 rb + i16][32 kk + 8 g .. +7]
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        pop[rb][kk] = *(const lds_bf16x8*)(sp + pr_off + rb * 16 * PPITCH + 64 * kk);
+    bf16x8 vop[2][KK];
+    auto load_v = [&](bf16x8 (&dst)[KK], int dt) {
+      const int d16 = w * NDT + dt;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const uint32_t o0 = ub + 32768u * kk + 256u * (uint32_t)(d16 >> 3) + trb[0][d16 & 7];
+        const uint32_t o1 = ub + 32768u * kk + 256u * (uint32_t)(d16 >> 3) + trb[1][d16 & 7];
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sb + o0));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sb + o1));
+        dst[kk] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    };
+    load_v(vop[0], 0);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      if (dt + 1 < NDT) load_v(vop[(dt + 1) & 1], dt + 1);
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) mfma16_acc(o[dt][rb], vop[dt & 1][kk], pop[rb][kk]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
-  for (int j = 0; j < n_my; j += 2) {
-    process(kA, j);
-    if (j + 1 < n_my) process(kB, j + 1);
+  // ---- the pipeline: NBUF - 1 units in flight ahead of the one computed.
+  // A second pass runs only if some row's scores jumped past kMaxJump.
+  constexpr int AHEAD = NBUF - 1;
+#pragma nounroll
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) o[dt][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int rb = 0; rb < QRB; ++rb) {
+      mref[rb] = -INFINITY;
+      mtrue[rb] = -INFINITY;
+      lround[rb] = lexact[rb] = 0.f;
+    }
+    jumped = false;
+    int ops_ring[NBUF];   // DMA count per in-flight unit, indexed by u % NBUF
+#pragma unroll
+    for (int j = 0; j < NBUF; ++j) ops_ring[j] = 0;
+    if (n_units > 0) {
+      issue_unit(0);
+      ops_ring[0] = unit_ops(0);
+    }
+    if constexpr (KS) {
+      if (pass == 0) {
+        // Q tile rows -> the last staging buffer (free until unit NBUF-1),
+        // swizzled like key rows so the operand reads below match the K reads
+        const uint32_t qb = (uint32_t)(NBUF - 1) * (UK * 1024);
+#pragma unroll
+        for (int i = 0; i < RT / 4; ++i) {
+          const int r = w + 4 * i;
+          const uint16_t* src = a.q + ((size_t)b * a.R + min(row0 + r, a.R - 1)) * D;
+          dma_row16(src, 16u * (uint32_t)(lane ^ swz16(r & 15)), lds0 + qb + (uint32_t)r * 1024u);
+        }
+      }
+    }
+    // The compiler counts only its own loads (Q, bounds, page ids), not the
+    // staging DMAs above.  Draining everything here, where unit 0 has to land
+    // anyway, leaves it no reason to wait on the memory counter inside the
+    // key loop, where such a wait would also stall on the prefetched units.
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    if constexpr (KS) {
+      if (pass == 0) {
+        asm volatile("s_barrier" ::: "memory");   // every wave's Q rows landed
+        const uint32_t qb = (uint32_t)(NBUF - 1) * (UK * 1024);
+#pragma unroll
+        for (int rb = 0; rb < QRB; ++rb)
+#pragma unroll
+          for (int ks = 0; ks < 16; ++ks)
+            qreg[rb][ks] = *(const lds_bf16x8*)(sb + qb + qkb[ks & 3] + 64 * (ks & 12) + 16384 * rb);
+        // the first wait_vm_barrier below (lgkmcnt(0) + barrier) retires these
+        // reads before unit NBUF-1 is staged into the same buffer
+      }
+    }
+    for (int u = 1; u < AHEAD && u < n_units; ++u) {
+      issue_unit(u);
+      ops_ring[u % NBUF] = unit_ops(u);
+    }
+    for (int u = 0; u < n_units; ++u) {
+      int newer = 0;   // DMA ops issued after unit u's
+#pragma unroll
+      for (int j = 1; j < AHEAD; ++j) newer += (u + j < n_units) ? ops_ring[(u + j) % NBUF] : 0;
+      wait_vm_barrier(__builtin_amdgcn_readfirstlane(newer));   // unit u staged; unit u-1 no longer read
+      if (u + AHEAD < n_units) {
+        issue_unit(u + AHEAD);
+        ops_ring[(u + AHEAD) % NBUF] = unit_ops(u + AHEAD);
+      }
+      compute_unit(u, pass);
+    }
+    // MFMA write -> VALU write of the same accumulator (a second pass clears
+    // the tile): 24 wait states.  The clear sits behind the branch below.
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    if (pass == 1) break;
+    if (tid == 0) *sm_redo = 0;
+    __syncthreads();   // every wave is done with the buffers and has read the flag's old value
+    if (__any(jumped) && lane == 0) *sm_redo = 1;
+    __syncthreads();
+    if (*sm_redo == 0) break;
+    // second pass: every row's reference is its true maximum over the item
+#pragma unroll
+    for (int rb = 0; rb < QRB; ++rb) mpreset[rb] = mtrue[rb];
+    row_reduce_max(mpreset);
+  }
+  // accumulators of the last 8 PV MFMAs: 8 more wait states each, in write order
+  {
+    constexpr int LAST = (8 + NRB * KK - 1) / (NRB * KK);   // trailing dim blocks to settle
+#pragma unroll
+    for (int dt = NDT - LAST; dt < NDT; ++dt)
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) settle_acc(o[dt][rb]);
   }
 
-  // ---- denominators: lanes of a row (4 groups) then the 4 waves
+  // ---- row statistics: the QK waves publish (ref, sums) per row
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    float lr = lround[nt], le = lexact[nt];
+  for (int rb = 0; rb < QRB; ++rb) {
+    float lr = lround[rb], le = lexact[rb];
     lr += __shfl_xor(lr, 16);
     lr += __shfl_xor(lr, 32);
     le += __shfl_xor(le, 16);
     le += __shfl_xor(le, 32);
     if (g == 0) {
-      sm.lsum[0][w][nt * 16 + i16] = lr;
-      sm.lsum[1][w][nt * 16 + i16] = le;
+      const int row = qrow(rb);
+      const int slot = KS ? w : 0;
+      if (slot == 0) st_m[row] = mref[rb];
+      st_lr[slot * RT + row] = lr;
+      st_le[slot * RT + row] = le;
     }
   }
   __syncthreads();
+
+  // ---- finalize: (-inf, 0) for rows without a visible key; each wave writes
+  // its latent dims of every row, wave 0 the LSEs
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    if (!rvalid[nt]) continue;
-    const int r = nt * 16 + i16;
-    const float lr = sm.lsum[0][0][r] + sm.lsum[0][1][r] + sm.lsum[0][2][r] + sm.lsum[0][3][r];
-    const float le = sm.lsum[1][0][r] + sm.lsum[1][1][r] + sm.lsum[1][2][r] + sm.lsum[1][3][r];
-    const bool empty = !(lr > 0.f);   // the row max contributes P = 1 whenever a key is visible
+  for (int rb = 0; rb < NRB; ++rb) {
+    const int row = rb * 16 + i16;
+    float lr = 0.f, le = 0.f;
+#pragma unroll
+    for (int k = 0; k < NSLOT; ++k) {
+      lr += st_lr[k * RT + row];
+      le += st_le[k * RT + row];
+    }
+    const bool empty = !(lr > 0.f);   // a visible key contributes P >= 1 (its max set the reference)
     const float inv = empty ? 0.f : 1.f / lr;
-    const float lse_val = empty ? -INFINITY : (m[nt] + log2f(le)) * kLn2;
-    const size_t row_g = (size_t)b * a.R + row0 + r;
+    const bool store = row0 + row < a.R;
+    const size_t row_g = (size_t)b * a.R + row0 + row;
     if (a.direct) {
       uint16_t* dst = a.out_lat + row_g * D + 128 * w + 4 * g;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
+      for (int dt = 0; dt < NDT; ++dt) {
+        const f32x4 v = o[dt][rb] * inv;
         uint2 wv;
-        wv.x = bf16_rne(o[dt][nt][0] * inv) | (bf16_rne(o[dt][nt][1] * inv) << 16);
-        wv.y = bf16_rne(o[dt][nt][2] * inv) | (bf16_rne(o[dt][nt][3] * inv) << 16);
-        *reinterpret_cast<uint2*>(dst + 16 * dt) = wv;
+        wv.x = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
+        wv.y = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
+        if (store) *reinterpret_cast<uint2*>(dst + 16 * dt) = wv;
       }
-      if (w == 0 && g == 0) a.lse[row_g] = lse_val;
+      if (store && w == 0 && g == 0)
+        a.lse[row_g] = empty ? -INFINITY : (st_m[row] + log2f(le)) * kLn2;
     } else {
       const size_t prow = (size_t)s * a.B * a.R + row_g;
-      if (w == 0 && g == 0) a.part_lse[prow] = lse_val;
-      if (empty) continue;   // the merge never reads partials with lse = -inf
-      float* dst = a.part_o + prow * D + 128 * w + 4 * g;
+      if (store && w == 0 && g == 0)
+        a.part_lse[prow] = empty ? -INFINITY : (st_m[row] + log2f(le)) * kLn2;
+      if (empty || !store) continue;   // the merge never reads partials with lse = -inf
+      uint16_t* dst = a.part_o + prow * D + 128 * w + 4 * g;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4*>(dst + 16 * dt) = o[dt][nt] * inv;
+      for (int dt = 0; dt < NDT; ++dt) {
+        const f32x4 v = o[dt][rb] * inv;
+        uint2 wv;
+        wv.x = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
+        wv.y = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
+        *reinterpret_cast<uint2*>(dst + 16 * dt) = wv;
+      }
     }
   }
 }
 
 // LSE merge of the S partials of one row, computed by one wave (lane owns
 // dims 8*lane .. 8*lane+7).  The split LSEs are read in one round (lane s
-// holds split s), then the non-empty partials are fetched eight at a time
-// with all loads in flight together.  Partials of empty splits are never
-// read (their workspace bytes may be stale).  Returns the row's lse.
-__device__ __forceinline__ float merge_row(const float* __restrict__ part_o,
+// holds split s), then the non-empty partials (bf16, normalised) are fetched
+// eight at a time with all loads in flight together.  Partials of empty
+// splits are never read (their workspace bytes may be stale).  Returns the
+// row's lse; (-inf, 0) when no split saw a key.
+__device__ __forceinline__ float merge_row(const uint16_t* __restrict__ part_o,
                                            const float* __restrict__ part_lse, int S,
                                            size_t stride_rows, size_t row, int lane, float out[8]) {
   float acc[8];
@@ -383,27 +718,24 @@ __device__ __forceinline__ float merge_row(const float* __restrict__ part_o,
     for (int off = 32; off >= 1; off >>= 1) total += __shfl_xor(total, off);
   }
   for (int s0 = 0; s0 < S; s0 += 8) {
-    f32x4 v[8][2];
+    uint4 v[8];
     float ws[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int sj = s0 + j;
       ws[j] = __shfl(wl, sj < S ? sj : 0);
       ws[j] = sj < S ? ws[j] : 0.f;
-      if (ws[j] > 0.f) {   // wave-uniform
-        const f32x4* src = reinterpret_cast<const f32x4*>(part_o + ((size_t)sj * stride_rows + row) * D + lane * 8);
-        v[j][0] = src[0];
-        v[j][1] = src[1];
-      } else {
-        v[j][0] = v[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+      v[j] = ws[j] > 0.f   // wave-uniform
+                 ? *reinterpret_cast<const uint4*>(part_o + ((size_t)sj * stride_rows + row) * D + lane * 8)
+                 : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
+      const uint32_t wd[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        acc[e] += ws[j] * v[j][0][e];
-        acc[4 + e] += ws[j] * v[j][1][e];
+        acc[2 * e] += ws[j] * bf16_to_f32(wd[e] & 0xFFFFu);
+        acc[2 * e + 1] += ws[j] * bf16_to_f32(wd[e] >> 16);
       }
     }
   }
@@ -413,7 +745,7 @@ __device__ __forceinline__ float merge_row(const float* __restrict__ part_o,
   return mx + logf(total);
 }
 
-__global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restrict__ part_o,
+__global__ __launch_bounds__(kThreads) void combine_kernel(const uint16_t* __restrict__ part_o,
                                                            const float* __restrict__ part_lse,
                                                            uint16_t* __restrict__ out_lat,
                                                            float* __restrict__ lse, int rows, int S) {
@@ -436,7 +768,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restri
 // wave computes out[16 rows][128] = o_lat[16][512] . W_UV[h]^T on MFMA and
 // applies sigmoid(gate).
 __global__ __launch_bounds__(kThreads) void gated_epilogue_kernel(
-    const float* __restrict__ part_o, const float* __restrict__ part_lse,
+    const uint16_t* __restrict__ part_o, const float* __restrict__ part_lse,
     const uint16_t* __restrict__ w_uv, const uint16_t* __restrict__ gate,
     uint16_t* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ out_lat,
     int BT, int H, int S) {
@@ -551,10 +883,16 @@ int ensure_device() {
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MLA_ERR_HIP;
     const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
     if (ok) {
-      if (hipFuncSetAttribute(reinterpret_cast<const void*>(verify_attn_kernel),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(AttnSmem)) != hipSuccess ||
-          hipFuncSetAttribute(reinterpret_cast<const void*>(gated_epilogue_kernel),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 64 * 1024) != hipSuccess)
+      const void* attn[] = {reinterpret_cast<const void*>(attn_kernel<0>),
+                            reinterpret_cast<const void*>(attn_kernel<1>),
+                            reinterpret_cast<const void*>(attn_kernel<2>)};
+      bool fail = false;
+      for (const void* f : attn)
+        fail |= hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kAttnSmemBytes) !=
+                hipSuccess;
+      fail |= hipFuncSetAttribute(reinterpret_cast<const void*>(gated_epilogue_kernel),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, 64 * 1024) != hipSuccess;
+      if (fail)
         return MLA_ERR_HIP;
     }
     st = ok ? 1 : -1;
@@ -588,15 +926,23 @@ int run_attention(const mla_verify_params* p, const mla::Plan& pl, const mla_bf1
   a.direct = pl.use_partials ? 0 : 1;
   const size_t total_rows = (size_t)p->batch * pl.rows;
   if (pl.use_partials) {
-    a.part_o = static_cast<float*>(ws);
-    a.part_lse = a.part_o + (size_t)pl.splits * total_rows * D;
+    a.part_o = static_cast<uint16_t*>(ws);
+    a.part_lse = reinterpret_cast<float*>(a.part_o + (size_t)pl.splits * total_rows * D);
   } else {
     a.out_lat = out_lat;
     a.lse = lse;
   }
   const size_t items = (size_t)p->batch * pl.row_tiles * pl.splits;
   const unsigned grid = (unsigned)((items + mla::kNumXCDs - 1) / mla::kNumXCDs * mla::kNumXCDs);
-  hipLaunchKernelGGL(verify_attn_kernel, dim3(grid), dim3(kThreads), sizeof(AttnSmem), stream, a);
+  const int mode = pl.shape.mode;
+  if (mode == 0)
+    hipLaunchKernelGGL((attn_kernel<0>), dim3(grid), dim3(256), kAttnSmemBytes, stream, a);
+  else if (mode == 1)
+    hipLaunchKernelGGL((attn_kernel<1>), dim3(grid), dim3(256), kAttnSmemBytes, stream, a);
+  else if (mode == 2)
+    hipLaunchKernelGGL((attn_kernel<2>), dim3(grid), dim3(256), kAttnSmemBytes, stream, a);
+  else
+    return MLA_ERR_SHAPE;
   return launch_status();
 }
 
@@ -634,8 +980,8 @@ int mla_verify_attn(const mla_verify_params* p, const mla_bf16* q_latent,
                      workspace, st);
   if (rc != MLA_OK || !pl.use_partials) return rc;
   const int rows = p->batch * pl.rows;
-  const float* part_o = static_cast<const float*>(workspace);
-  const float* part_lse = part_o + (size_t)pl.splits * rows * D;
+  const uint16_t* part_o = static_cast<const uint16_t*>(workspace);
+  const float* part_lse = reinterpret_cast<const float*>(part_o + (size_t)pl.splits * rows * D);
   hipLaunchKernelGGL(combine_kernel, dim3((rows + 3) / 4), dim3(kThreads), 0, st, part_o, part_lse,
                      out_latent, lse, rows, pl.splits);
   return launch_status();
@@ -664,8 +1010,8 @@ int mla_verify_attn_gated(const mla_verify_params* p, const mla_bf16* q_latent,
   if (rc != MLA_OK) return rc;
   const int bt_rows = p->batch * p->q_len;
   const int rows = bt_rows * p->num_heads;
-  const float* part_o = static_cast<const float*>(workspace);
-  const float* part_lse = part_o + (size_t)pl.splits * rows * D;
+  const uint16_t* part_o = static_cast<const uint16_t*>(workspace);
+  const float* part_lse = reinterpret_cast<const float*>(part_o + (size_t)pl.splits * rows * D);
   const unsigned grid = (unsigned)(((bt_rows + 63) / 64) * p->num_heads);
   hipLaunchKernelGGL(gated_epilogue_kernel, dim3(grid), dim3(kThreads), 64 * 1024, st, part_o,
                      part_lse, w_uv, gate_logits, out, lse, out_latent, bt_rows, p->num_heads,
