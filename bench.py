@@ -1,24 +1,42 @@
 #!/usr/bin/env python3
 """Benchmark: speculative-verify attention (gated NoPE MLA, absorbed) on one MI355X.
 
-A step is one verify call over one batch of the TP8-share workload (16
-requests, 8 heads, k = 7 draft tokens so q_len 8, 512-d bf16 latent cache,
-contexts uniform in [1024, 1536], 64-token pages scattered in a 4096-page
-pool).  Inputs are resident in HBM when timing starts.  To keep the 256 MB
-Infinity Cache from serving the KV, consecutive steps rotate over enough
-identical copies of the page pool (each at its own address) that the bytes
-one cycle touches exceed twice the cache ("cold").  --warm uses one copy.
+A step is one verify call over one batch of synthetic input of the chosen
+workload (default: the TP8-share workload -- 16 requests, 8 heads, k = 7
+draft tokens so q_len 8, 512-d bf16 latent cache, contexts uniform in
+[1024, 1536], 64-token pages scattered in a 4096-page pool).  Inputs are
+resident in HBM when timing starts.  To keep the 256 MB Infinity Cache from
+serving the KV, consecutive calls rotate over enough identical copies of the
+page pool (each at its own address) that the bytes one cycle touches exceed
+twice the cache ("cold"); --warm uses one copy.  Calls are captured into a
+hipGraph and replayed (--eager times plain launches).
 
-Prints one JSON line.  ``roofline`` is for the attention call (attention
-kernel plus the split combine when there is one): algorithmic bytes per call
-over the average call duration measured with HIP events on the launch stream.
-``cpu_baseline`` times the float64 CPU oracle on a bounded sample of the same
-workload.
+Prints one JSON line:
+  value      verify tokens/s of the whole call (every kernel of the call);
+  roofline   the dominant kernel -- the attention kernel, launched on its
+             own through mla_verify_attn_partials (or mla_verify_attn when
+             the call is that single kernel) -- as algorithmic bytes (or
+             flops) per launch over its average duration, measured with HIP
+             events on the stream it is launched on; `traffic` is the HBM
+             traffic rocprofv3 counted for that kernel (FETCH_SIZE +
+             WRITE_SIZE, scaled by the same counters' reading for a copy of
+             known size), reported only while the kernel source is the one
+             that was counted;
+  cpu_baseline  the float64 CPU oracle on a bounded sample of the workload.
+
+Other modes:
+  --copy-probe         also launch a 1 GiB device copy (counter calibration)
+  --pmc-report DIR     turn rocprofv3 counter CSVs (FETCH_SIZE run in
+                       DIR/fetch, WRITE_SIZE run in DIR/write) into the
+                       traffic record profiles/traffic_config<N>.json
 """
 from __future__ import annotations
 
 import argparse
+import csv
 import ctypes
+import glob
+import hashlib
 import json
 import math
 import os
@@ -33,6 +51,9 @@ METRIC = "verify tokens/s + % of binding roofline (HBM GB/s or bf16 MFMA) on 1 M
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
 MALL_BYTES = 256 << 20
+COPY_PROBE_BYTES = 1 << 30
+KERNEL_SOURCE = os.path.join(ROOT, "speculative_verify_attention_absorbed_amd", "csrc",
+                             "mla_verify_kernels.hip")
 
 WORKLOAD_NAMES = {
     1: "tiny verify B=1 H=8 q_len=4 ctx=256 gated",
@@ -43,8 +64,15 @@ WORKLOAD_NAMES = {
 }
 
 
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
 def algorithmic(x, gated):
-    """Bytes and flops the method must move/do per call (visible keys only)."""
+    """Bytes and flops the method must move / do per call (visible keys only):
+    the KV of each request read once, Q, the outputs, the LSEs, the tables;
+    for the gated call also W_UV and the gate."""
     import numpy as np
     b, t, h = x.shape
     r = t * h
@@ -69,8 +97,7 @@ def algorithmic(x, gated):
 
 def cpu_baseline(x, seconds):
     """Time the float64 oracle (latent definition of the call) on whole batches
-    of the same workload until ~`seconds` of CPU time, at least once."""
-    import numpy as np
+    of the same workload until ~`seconds` of wall time, at least once."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -93,12 +120,68 @@ def cpu_baseline(x, seconds):
 
 
 def oracle_q_bits(x):
+    import numpy as np
     import oracle
     from verify_inputs import f32_to_bf16_bits
-    import numpy as np
     return f32_to_bf16_bits(oracle.absorb_query(x.q_nope, x.w_uk).astype(np.float32))
 
 
+# --------------------------------------------------------------- counters
+def _counter_rows(directory, counter):
+    rows = []
+    for f in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    rows.append(r)
+    return rows
+
+
+def _per_dispatch(rows, name_part):
+    acc = {}
+    for r in rows:
+        if name_part in r["Kernel_Name"]:
+            acc[r["Dispatch_Id"]] = acc.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    return acc
+
+
+def pmc_report(directory, config):
+    """Calibrated HBM traffic of the attention kernel from two counter runs."""
+    out = {"config": config, "kernel_source_sha": kernel_source_hash()}
+    for counter, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+        rows = _counter_rows(os.path.join(directory, sub), counter)
+        copy = _per_dispatch(rows, "copy") or _per_dispatch(rows, "elementwise")
+        attn = _per_dispatch(rows, "attn_kernel")
+        if not copy or not attn:
+            raise SystemExit(f"{counter}: missing copy probe or attention dispatches in {sub}")
+        copy_kib = max(copy.values())          # the 1 GiB probe is the largest copy
+        factor = COPY_PROBE_BYTES / (copy_kib * 1024.0)
+        vals = sorted(attn.values())
+        med = vals[len(vals) // 2]
+        out[counter.lower()] = {"raw_kib_per_dispatch": med, "copy_probe_raw_kib": copy_kib,
+                                "factor": round(factor, 4),
+                                "bytes_per_dispatch": round(med * 1024.0 * factor)}
+    out["traffic_bytes"] = out["fetch_size"]["bytes_per_dispatch"] + \
+        out["write_size"]["bytes_per_dispatch"]
+    path = os.path.join(ROOT, "profiles", f"traffic_config{config}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
+def recorded_traffic(config):
+    path = os.path.join(ROOT, "profiles", f"traffic_config{config}.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha") != kernel_source_hash():
+        return None        # counted on another version of the kernel
+    return rec.get("traffic_bytes")
+
+
+# --------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -110,7 +193,13 @@ def main():
     ap.add_argument("--warm", action="store_true", help="one pool copy (cache-warm)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--pmc-report", metavar="DIR")
     args = ap.parse_args()
+
+    if args.pmc_report:
+        pmc_report(args.pmc_report, args.config)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -129,6 +218,13 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     lib = mv.load_library()
+
+    if args.copy_probe:      # counter calibration: one copy of known size
+        src = torch.empty(COPY_PROBE_BYTES // 2, dtype=torch.int16, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     x = make_config(args.config)
     b, t, h = x.shape
@@ -158,42 +254,62 @@ def main():
     s_used = mv.verify_num_splits(params, gated)
     ws_bytes = mv.verify_workspace_size(params, gated)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    rows = b * t * h
     if gated:
         out = torch.empty((b, t, h, 128), dtype=torch.bfloat16, device=dev)
     else:
         out = torch.empty((b, t, h, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((b, t, h), dtype=torch.float32, device=dev)
+    # the attention kernel alone: partials (split or gated calls) or the whole
+    # call when it is that single kernel
+    attn_alone_is_call = (not gated) and s_used == 1
+    part_o = torch.empty((s_used, rows, 512), dtype=torch.bfloat16, device=dev)
+    part_lse = torch.empty((s_used, rows), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
     vp = ctypes.c_void_p
     pref = ctypes.byref(params)
 
-    def call(i, stream_handle):
+    def call(i, sh):
         pool = pools[i % n_sets]
         if gated:
             rc = lib.mla_verify_attn_gated(pref, vp(q_lat.data_ptr()), vp(pool.data_ptr()),
                                            vp(bt.data_ptr()), vp(bounds.data_ptr()),
                                            vp(w_uv.data_ptr()), vp(gate.data_ptr()),
                                            vp(out.data_ptr()), vp(lse.data_ptr()), vp(0),
-                                           vp(ws.data_ptr()), ctypes.c_size_t(ws_bytes),
-                                           stream_handle)
+                                           vp(ws.data_ptr()), ctypes.c_size_t(ws_bytes), sh)
         else:
             rc = lib.mla_verify_attn(pref, vp(q_lat.data_ptr()), vp(pool.data_ptr()),
                                      vp(bt.data_ptr()), vp(bounds.data_ptr()), vp(out.data_ptr()),
                                      vp(lse.data_ptr()), vp(ws.data_ptr()),
-                                     ctypes.c_size_t(ws_bytes), stream_handle)
+                                     ctypes.c_size_t(ws_bytes), sh)
         if rc != 0:
             raise mv.MlaVerifyError(rc, "bench call")
 
-    stream = torch.cuda.current_stream()
-    sh = vp(stream.cuda_stream)
-    for i in range(max(args.warmup, 1)):
-        call(i, sh)
-    torch.cuda.synchronize()
+    def attn_only(i, sh):
+        pool = pools[i % n_sets]
+        rc = lib.mla_verify_attn_partials(pref, vp(q_lat.data_ptr()), vp(pool.data_ptr()),
+                                          vp(bt.data_ptr()), vp(bounds.data_ptr()),
+                                          vp(part_o.data_ptr()), vp(part_lse.data_ptr()), sh)
+        if rc != 0:
+            raise mv.MlaVerifyError(rc, "bench attention kernel")
 
-    mode = "eager"
-    graph = None
-    if not args.eager:
+    def timed(fn, steps, warmup):
+        """Average ms per `fn` call: W warm-up calls, then `steps` calls
+        bracketed by HIP events on the stream they run on."""
+        stream = torch.cuda.current_stream()
+        sh = vp(stream.cuda_stream)
+        for i in range(max(warmup, 1)):
+            fn(i, sh)
+        torch.cuda.synchronize()
+        if args.eager:
+            start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            start.record(stream)
+            for i in range(steps):
+                fn(i, sh)
+            end.record(stream)
+            torch.cuda.synchronize()
+            return start.elapsed_time(end) / steps, steps, "eager"
         # capture one rotation cycle (n_sets calls, at least 8) and replay it
         per_graph = n_sets * max(1, math.ceil(8 / n_sets))
         g = torch.cuda.CUDAGraph()
@@ -203,46 +319,44 @@ def main():
             with torch.cuda.graph(g, stream=cap):
                 csh = vp(torch.cuda.current_stream().cuda_stream)
                 for i in range(per_graph):
-                    call(i, csh)
+                    fn(i, csh)
         stream.wait_stream(cap)
         torch.cuda.synchronize()
-        graph = (g, per_graph)
-        mode = f"hipGraph replay ({per_graph} calls per graph)"
-        for _ in range(max(1, args.warmup // per_graph)):
+        for _ in range(max(1, warmup // per_graph)):
             g.replay()
         torch.cuda.synchronize()
-
-    # ---- timed region: exactly `steps` calls
-    steps = args.steps
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    if graph is None:
+        n_rep = max(1, round(steps / per_graph))
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         start.record(stream)
-        for i in range(steps):
-            call(i, sh)
-        end.record(stream)
-    else:
-        g, per_graph = graph
-        steps = per_graph * max(1, round(args.steps / per_graph))
-        start.record(stream)
-        for _ in range(steps // per_graph):
+        for _ in range(n_rep):
             g.replay()
         end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / steps
+        torch.cuda.synchronize()
+        return (start.elapsed_time(end) / (n_rep * per_graph), n_rep * per_graph,
+                f"hipGraph replay ({per_graph} calls per graph)")
+
+    # ---- timed region 1: exactly `steps` whole calls
+    ms, steps, mode = timed(call, args.steps, args.warmup)
     sec = ms * 1e-3
+    # ---- timed region 2: the attention kernel alone (same launch configuration)
+    if attn_alone_is_call:
+        kms = ms
+    else:
+        kms, _, _ = timed(attn_only, args.steps, args.warmup)
+    ksec = kms * 1e-3
 
     tokens = b * t
-    achieved_gbs = alg["bytes"] / sec / 1e9
-    achieved_tflops = alg["flops"] / sec / 1e12
     bound = "mfma" if args.config == 5 else "hbm"
+    k_gbs = alg["bytes"] / ksec / 1e9
+    k_tflops = alg["flops"] / ksec / 1e12
+    traffic = recorded_traffic(args.config)
     if bound == "hbm":
-        roof = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": None}
+        roof = {"bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
     else:
-        roof = {"bound": "mfma", "achieved": round(achieved_tflops, 2),
-                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+        roof = {"bound": "mfma", "achieved": round(k_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(k_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": traffic}
 
     rec = {
         "metric": METRIC,
@@ -262,11 +376,16 @@ def main():
                    "cache": "warm" if args.warm else f"cold: {n_sets} rotating pool copies",
                    "launch": mode},
         "roofline": roof,
-        "extra": {"algorithmic_bytes": alg["bytes"], "kv_bytes": alg["kv_bytes"],
-                  "flops": alg["flops"], "attention_tflops": round(achieved_tflops, 3),
-                  "kv_gbs": round(alg["kv_bytes"] / sec / 1e9, 1),
-                  "mfma_frac": round(achieved_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                  "hbm_frac": round(achieved_gbs / HBM_PEAK_GBS, 4)},
+        "extra": {"attention_kernel_us": round(kms * 1e3, 3),
+                  "call_us": round(ms * 1e3, 3),
+                  "algorithmic_bytes": alg["bytes"], "kv_bytes": alg["kv_bytes"],
+                  "flops": alg["flops"],
+                  "call_hbm_gbs": round(alg["bytes"] / sec / 1e9, 1),
+                  "call_hbm_frac": round(alg["bytes"] / sec / 1e9 / HBM_PEAK_GBS, 4),
+                  "kernel_attention_tflops": round(k_tflops, 3),
+                  "kernel_mfma_frac": round(k_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                  "kernel_kv_gbs": round(alg["kv_bytes"] / ksec / 1e9, 1),
+                  "kernel_source_sha": kernel_source_hash()},
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)

@@ -140,6 +140,38 @@ int mla_verify_attn(const mla_verify_params* p,
                     void* workspace, size_t workspace_bytes,
                     void* stream);
 
+/* The attention half of mla_verify_attn on its own: the S = mla_verify_num_splits(p, 0)
+ * split-KV results, for a caller that merges them itself (for example after
+ * exchanging them between ranks that hold different pages of one request).
+ *   part_o    [S, B*T*H, 512] bf16  split s's output, normalised by split s's
+ *                                   own softmax sum; rows whose split sees no
+ *                                   key are left unwritten
+ *   part_lse  [S, B*T*H]      fp32  split s's natural-log LSE (-inf: no key)
+ * Combining: lse = ln sum_s exp(lse_s), out = sum_s exp(lse_s - lse) part_o_s
+ * (mla_verify_lse_combine).  Errors as mla_verify_attn. */
+int mla_verify_attn_partials(const mla_verify_params* p,
+                             const mla_bf16* q_latent,
+                             const mla_bf16* latent_kv_pages,
+                             const int32_t* block_table,
+                             const int32_t* kv_bounds,
+                             mla_bf16* part_o,
+                             float* part_lse,
+                             void* stream);
+
+/* LSE combine ("Kimi K3: DSpark speculative decoding under Helix CP",
+ * "Changes": partial results merged through their softmax statistics, with
+ * (-inf, 0) as the identity).  rows = B*T*H, num_splits = S in 1..64;
+ * layouts as mla_verify_attn_partials; writes out_latent [rows, 512] bf16 and
+ * lse [rows] fp32; a row with no visible key in any split gets (-inf, 0).
+ * MLA_ERR_ARG / MLA_ERR_NULL on bad arguments (host checks), else as
+ * mla_verify_attn. */
+int mla_verify_lse_combine(int num_splits, int rows,
+                           const mla_bf16* part_o,
+                           const float* part_lse,
+                           mla_bf16* out_latent,
+                           float* lse,
+                           void* stream);
+
 /* Verify attention with the fused LSE combine + W_UV + sigmoid-gate epilogue
  * (vLLM drafter docstring: "LSE combine + W_UV"; the gate of "gated NoPE
  * MLA" read as an elementwise sigmoid over the 128-d per-head output).

@@ -10,6 +10,8 @@ Entry points (same names as the C ABI, without the ``mla_`` prefix):
     verify_attn(...)        -> (out_latent [B,T,H,512] bf16, lse [B,T,H] f32)
     verify_attn_gated(...)  -> (out [B,T,H,128] bf16, lse, out_latent or None)
     verify_absorb_q(...)    -> q_latent [B,T,H,512] bf16
+    verify_attn_partials(...) -> (part_o [S,B*T*H,512] bf16, part_lse [S,B*T*H] f32)
+    verify_lse_combine(...) -> (out_latent [rows,512] bf16, lse [rows] f32)
     verify_check / verify_num_splits / verify_workspace_size / status_string
 """
 from __future__ import annotations
@@ -21,7 +23,8 @@ import os
 __all__ = [
     "MlaVerifyError", "VerifyParams", "lib_path", "load_library", "verify_check",
     "verify_num_splits", "verify_workspace_size", "verify_attn", "verify_attn_gated",
-    "verify_absorb_q", "status_string", "EXPORTED_SYMBOLS",
+    "verify_absorb_q", "verify_attn_partials", "verify_lse_combine", "status_string",
+    "EXPORTED_SYMBOLS",
 ]
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -35,7 +38,8 @@ LATENT, PAGE, NOPE = 512, 64, 128
 
 EXPORTED_SYMBOLS = [
     "mla_verify_check", "mla_verify_num_splits", "mla_verify_workspace_size",
-    "mla_verify_attn", "mla_verify_attn_gated", "mla_verify_absorb_q",
+    "mla_verify_attn", "mla_verify_attn_partials", "mla_verify_lse_combine",
+    "mla_verify_attn_gated", "mla_verify_absorb_q",
     "mla_verify_status_string",
 ]
 
@@ -92,6 +96,10 @@ def load_library():
     lib.mla_verify_attn.restype = ctypes.c_int
     lib.mla_verify_attn_gated.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.mla_verify_attn_gated.restype = ctypes.c_int
+    lib.mla_verify_attn_partials.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
+    lib.mla_verify_attn_partials.restype = ctypes.c_int
+    lib.mla_verify_lse_combine.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp]
+    lib.mla_verify_lse_combine.restype = ctypes.c_int
     lib.mla_verify_absorb_q.argtypes = [P, vp, vp, vp, vp]
     lib.mla_verify_absorb_q.restype = ctypes.c_int
     lib.mla_verify_status_string.argtypes = [ctypes.c_int]
@@ -247,6 +255,59 @@ def verify_attn_gated(q_latent, latent_kv_pages, block_table, kv_bounds, w_uv, g
         _ptr(workspace), ctypes.c_size_t(nbytes), _stream(stream))
     _check(rc, "mla_verify_attn_gated")
     return out, lse, out_latent
+
+
+def verify_attn_partials(q_latent, latent_kv_pages, block_table, kv_bounds, sm_scale, *,
+                         num_splits=0, part_o=None, part_lse=None, stream=None,
+                         kv_dtype=KV_BF16):
+    """``mla_verify_attn_partials``: returns (part_o [S, B*T*H, 512] bf16,
+    part_lse [S, B*T*H] f32) with S = verify_num_splits(params)."""
+    torch = _torch()
+    params = _params_from(q_latent, latent_kv_pages, block_table, sm_scale, num_splits, kv_dtype)
+    _check(verify_check(params), "mla_verify_attn_partials")
+    b, t, h, d = q_latent.shape
+    bf = _bf16_types()
+    _dev_tensor(q_latent, "q_latent", (b, t, h, LATENT), bf)
+    _dev_tensor(latent_kv_pages, "latent_kv_pages", (latent_kv_pages.shape[0], PAGE, LATENT), bf)
+    _dev_tensor(block_table, "block_table", (b, block_table.shape[1]), (torch.int32,))
+    _dev_tensor(kv_bounds, "kv_bounds", (b, t), (torch.int32,))
+    s = verify_num_splits(params)
+    rows = b * t * h
+    dev = q_latent.device
+    if part_o is None:
+        part_o = torch.empty((s, rows, LATENT), dtype=torch.bfloat16, device=dev)
+    if part_lse is None:
+        part_lse = torch.empty((s, rows), dtype=torch.float32, device=dev)
+    _dev_tensor(part_o, "part_o", (s, rows, LATENT), bf)
+    _dev_tensor(part_lse, "part_lse", (s, rows), (torch.float32,))
+    rc = load_library().mla_verify_attn_partials(
+        ctypes.byref(params), _ptr(q_latent), _ptr(latent_kv_pages), _ptr(block_table),
+        _ptr(kv_bounds), _ptr(part_o), _ptr(part_lse), _stream(stream))
+    _check(rc, "mla_verify_attn_partials")
+    return part_o, part_lse
+
+
+def verify_lse_combine(part_o, part_lse, *, out_latent=None, lse=None, stream=None):
+    """``mla_verify_lse_combine``: merges [S, rows, 512] partials into
+    (out_latent [rows, 512] bf16, lse [rows] f32)."""
+    torch = _torch()
+    bf = _bf16_types()
+    if part_o.dim() != 3 or part_lse.dim() != 2:
+        raise ValueError("part_o must be [S, rows, 512] and part_lse [S, rows]")
+    s, rows, _ = part_o.shape
+    _dev_tensor(part_o, "part_o", (s, rows, LATENT), bf)
+    _dev_tensor(part_lse, "part_lse", (s, rows), (torch.float32,))
+    dev = part_o.device
+    if out_latent is None:
+        out_latent = torch.empty((rows, LATENT), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((rows,), dtype=torch.float32, device=dev)
+    _dev_tensor(out_latent, "out_latent", (rows, LATENT), bf)
+    _dev_tensor(lse, "lse", (rows,), (torch.float32,))
+    rc = load_library().mla_verify_lse_combine(int(s), int(rows), _ptr(part_o), _ptr(part_lse),
+                                               _ptr(out_latent), _ptr(lse), _stream(stream))
+    _check(rc, "mla_verify_lse_combine")
+    return out_latent, lse
 
 
 def verify_absorb_q(q_nope, w_uk, *, q_latent=None, stream=None):

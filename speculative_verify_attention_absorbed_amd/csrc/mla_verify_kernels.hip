@@ -906,9 +906,11 @@ int launch_status() {
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
+// Launch the attention kernel.  With partials, part_o / part_lse receive the
+// S split results; otherwise out_lat / lse receive the final result (S == 1).
 int run_attention(const mla_verify_params* p, const mla::Plan& pl, const mla_bf16* q,
                   const mla_bf16* pool, const int32_t* bt, const int32_t* bounds, mla_bf16* out_lat,
-                  float* lse, void* ws, hipStream_t stream) {
+                  float* lse, bool partials, mla_bf16* part_o, float* part_lse, hipStream_t stream) {
   AttnArgs a{};
   a.q = q;
   a.pool = pool;
@@ -923,11 +925,10 @@ int run_attention(const mla_verify_params* p, const mla::Plan& pl, const mla_bf1
   a.S = pl.splits;
   a.row_tiles = pl.row_tiles;
   a.scale_log2 = p->sm_scale * kLog2e;
-  a.direct = pl.use_partials ? 0 : 1;
-  const size_t total_rows = (size_t)p->batch * pl.rows;
-  if (pl.use_partials) {
-    a.part_o = static_cast<uint16_t*>(ws);
-    a.part_lse = reinterpret_cast<float*>(a.part_o + (size_t)pl.splits * total_rows * D);
+  a.direct = partials ? 0 : 1;
+  if (partials) {
+    a.part_o = part_o;
+    a.part_lse = part_lse;
   } else {
     a.out_lat = out_lat;
     a.lse = lse;
@@ -976,14 +977,43 @@ int mla_verify_attn(const mla_verify_params* p, const mla_bf16* q_latent,
   rc = ensure_device();
   if (rc != MLA_OK) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  rc = run_attention(p, pl, q_latent, latent_kv_pages, block_table, kv_bounds, out_latent, lse,
-                     workspace, st);
-  if (rc != MLA_OK || !pl.use_partials) return rc;
   const int rows = p->batch * pl.rows;
-  const uint16_t* part_o = static_cast<const uint16_t*>(workspace);
-  const float* part_lse = reinterpret_cast<const float*>(part_o + (size_t)pl.splits * rows * D);
+  mla_bf16* part_o = static_cast<mla_bf16*>(workspace);
+  float* part_lse = reinterpret_cast<float*>(part_o + (size_t)pl.splits * rows * D);
+  rc = run_attention(p, pl, q_latent, latent_kv_pages, block_table, kv_bounds, out_latent, lse,
+                     pl.use_partials, part_o, part_lse, st);
+  if (rc != MLA_OK || !pl.use_partials) return rc;
   hipLaunchKernelGGL(combine_kernel, dim3((rows + 3) / 4), dim3(kThreads), 0, st, part_o, part_lse,
                      out_latent, lse, rows, pl.splits);
+  return launch_status();
+}
+
+int mla_verify_attn_partials(const mla_verify_params* p, const mla_bf16* q_latent,
+                             const mla_bf16* latent_kv_pages, const int32_t* block_table,
+                             const int32_t* kv_bounds, mla_bf16* part_o, float* part_lse,
+                             void* stream) {
+  int rc = mla::check_params(p);
+  if (rc != MLA_OK) return rc;
+  if (any_null({q_latent, latent_kv_pages, block_table, kv_bounds, part_o, part_lse})) return MLA_ERR_NULL;
+  if (any_misaligned({q_latent, latent_kv_pages, block_table, kv_bounds, part_o, part_lse}))
+    return MLA_ERR_ARG;
+  const mla::Plan pl = mla::make_plan(p, false);
+  rc = ensure_device();
+  if (rc != MLA_OK) return rc;
+  return run_attention(p, pl, q_latent, latent_kv_pages, block_table, kv_bounds, nullptr, nullptr,
+                       true, part_o, part_lse, static_cast<hipStream_t>(stream));
+}
+
+int mla_verify_lse_combine(int num_splits, int rows, const mla_bf16* part_o, const float* part_lse,
+                           mla_bf16* out_latent, float* lse, void* stream) {
+  if (num_splits < 1 || num_splits > MLA_VERIFY_MAX_SPLITS || rows < 1) return MLA_ERR_ARG;
+  if (any_null({part_o, part_lse, out_latent, lse})) return MLA_ERR_NULL;
+  if (any_misaligned({part_o, part_lse, out_latent, lse})) return MLA_ERR_ARG;
+  const int rc = ensure_device();
+  if (rc != MLA_OK) return rc;
+  hipLaunchKernelGGL(combine_kernel, dim3((rows + 3) / 4), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), part_o, part_lse, out_latent, lse, rows,
+                     num_splits);
   return launch_status();
 }
 
@@ -1005,13 +1035,13 @@ int mla_verify_attn_gated(const mla_verify_params* p, const mla_bf16* q_latent,
   rc = ensure_device();
   if (rc != MLA_OK) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  rc = run_attention(p, pl, q_latent, latent_kv_pages, block_table, kv_bounds, nullptr, nullptr,
-                     workspace, st);
-  if (rc != MLA_OK) return rc;
   const int bt_rows = p->batch * p->q_len;
   const int rows = bt_rows * p->num_heads;
-  const uint16_t* part_o = static_cast<const uint16_t*>(workspace);
-  const float* part_lse = reinterpret_cast<const float*>(part_o + (size_t)pl.splits * rows * D);
+  mla_bf16* part_o = static_cast<mla_bf16*>(workspace);
+  float* part_lse = reinterpret_cast<float*>(part_o + (size_t)pl.splits * rows * D);
+  rc = run_attention(p, pl, q_latent, latent_kv_pages, block_table, kv_bounds, nullptr, nullptr, true,
+                     part_o, part_lse, st);
+  if (rc != MLA_OK) return rc;
   const unsigned grid = (unsigned)(((bt_rows + 63) / 64) * p->num_heads);
   hipLaunchKernelGGL(gated_epilogue_kernel, dim3(grid), dim3(kThreads), 64 * 1024, st, part_o,
                      part_lse, w_uv, gate_logits, out, lse, out_latent, bt_rows, p->num_heads,

@@ -116,6 +116,16 @@ def test_entry_points_validate_before_any_hip_call(lib):
     assert lib.mla_verify_attn(ctypes.byref(p4), *args, fake, 16, z) == -5
     assert lib.mla_verify_attn_gated(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake,
                                      fake, z, z, 0, z) == -5
+    # partial-only and combine entry points
+    assert lib.mla_verify_attn_partials(ctypes.byref(p), fake, fake, fake, fake, z, fake, z) == -1
+    assert lib.mla_verify_attn_partials(ctypes.byref(p), fake, odd, fake, fake, fake, fake, z) == -4
+    assert lib.mla_verify_attn_partials(ctypes.byref(good(page_size=32)), fake, fake, fake, fake,
+                                        fake, fake, z) == -2
+    assert lib.mla_verify_lse_combine(0, 8, fake, fake, fake, fake, z) == -4
+    assert lib.mla_verify_lse_combine(65, 8, fake, fake, fake, fake, z) == -4
+    assert lib.mla_verify_lse_combine(4, 0, fake, fake, fake, fake, z) == -4
+    assert lib.mla_verify_lse_combine(4, 8, fake, z, fake, fake, z) == -1
+    assert lib.mla_verify_lse_combine(4, 8, fake, fake, odd, fake, z) == -4
     # bad params take precedence over everything else
     assert lib.mla_verify_attn(ctypes.byref(good(latent_dim=576)), z, *args[1:], z, 0, z) == -2
     assert lib.mla_verify_attn(None, *args, z, 0, z) == -1

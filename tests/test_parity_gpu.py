@@ -250,3 +250,47 @@ def test_fp8_request_raises():
     with pytest.raises(mv.MlaVerifyError, match="MLA_ERR_DTYPE"):
         mv.verify_attn(d["q_latent"], d["pool"], d["block_table"], d["kv_bounds"], x.sm_scale,
                        kv_dtype=mv.KV_FP8_E4M3)
+
+
+# ------------------------------------------------ partials + combine entry points
+@pytest.mark.parametrize("cfg,splits", [(3, 4), (2, 5)])
+def test_partials_match_oracle_chunks_and_combine_matches_call(cfg, splits):
+    """mla_verify_attn_partials: split s is attention over the keys of chunk s
+    (pages [floor(s n_pg / S), floor((s+1) n_pg / S)) of the request, clipped
+    to each token's bound); mla_verify_lse_combine of those partials gives
+    the same bits as mla_verify_attn."""
+    log(f"partials + combine: config {cfg} sharp, S={splits}")
+    x = make_config(cfg, sharp=True)
+    q_bits = oracle_qlat_bits(x)
+    d = upload(x, q_latent_bits=q_bits)
+    part_o, part_lse = mv.verify_attn_partials(d["q_latent"], d["pool"], d["block_table"],
+                                               d["kv_bounds"], x.sm_scale, num_splits=splits)
+    out, lse = mv.verify_attn(d["q_latent"], d["pool"], d["block_table"], d["kv_bounds"],
+                              x.sm_scale, num_splits=splits)
+    b, t, h = x.shape
+    comb, comb_lse = mv.verify_lse_combine(part_o, part_lse)
+    sync()
+    assert np.array_equal(bits_of(comb), bits_of(out).reshape(b * t * h, 512))
+    assert np.array_equal(comb_lse.cpu().numpy(), lse.cpu().numpy().reshape(-1))
+
+    po = f64_of(part_o).reshape(splits, b, t, h, 512)
+    pl = part_lse.cpu().numpy().astype(np.float64).reshape(splits, b, t, h)
+    q = oracle.bf16_to_f64(q_bits)
+    want_o, want_l, got_o, got_l = [], [], [], []
+    for bi in range(b):
+        c_b, n_b = oracle.request_keys(x.pool, x.block_table, x.kv_bounds, bi)
+        for s, (k0, k1) in enumerate(oracle.split_pages(n_b, splits)):
+            for ti in range(t):
+                L = oracle.token_bound(x.kv_bounds, bi, ti, n_b)
+                hi = min(k1, L)
+                for hh in range(h):
+                    o, l = oracle.attend_chunk(q[bi, ti, hh], c_b[k0:max(k0, hi)], x.sm_scale)
+                    if l == -np.inf:
+                        assert pl[s, bi, ti, hh] == -np.inf, (s, bi, ti, hh)
+                        continue
+                    want_o.append(o)
+                    want_l.append(l)
+                    got_o.append(po[s, bi, ti, hh])
+                    got_l.append(pl[s, bi, ti, hh])
+    assert_close_output(np.array(got_o), np.array(want_o), "partials")
+    assert np.abs(np.array(got_l) - np.array(want_l)).max() <= 1e-3
