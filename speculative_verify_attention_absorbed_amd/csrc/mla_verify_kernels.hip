@@ -260,6 +260,12 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   const int t_lo = row0 / a.H;
   const int ntok = (row0 + rows_here - 1) / a.H - t_lo + 1;
   const int tb = (lane < ntok) ? clampi(a.bounds[b * a.T + t_lo + lane], 0, max_keys) : 0;
+  // The request's whole block-table row, when it fits, is staged now, in the
+  // same memory round trip as the bounds (the split's page range is known
+  // only once the bounds are).
+  const bool whole_row = a.P <= mla::kMaxSplitPages;
+  if (whole_row)
+    for (int i = tid; i < a.P; i += 256) sm_pid[i] = a.bt[b * a.P + i];
 
   // ---- Q^T of this wave's QK rows.  Row-split tiles load their own rows
   // here (in flight while the first pages stream); key-split tiles, where
@@ -299,8 +305,16 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   const int k_end = min(p_end * PG, n_tile);
   const int n_units = k_end > k_begin ? (k_end - k_begin + UK - 1) / UK : 0;
 
-  for (int i = tid; i < p_end - p_begin; i += 256) sm_pid[i] = a.bt[b * a.P + p_begin + i];
+  if (!whole_row)
+    for (int i = tid; i < p_end - p_begin; i += 256) sm_pid[i] = a.bt[b * a.P + p_begin + i];
+  const int pid0 = whole_row ? p_begin : 0;   // sm_pid index of the split's first page
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+  // Lane offsets of the DMA of key row w + 4i: its chunk order is swizzled by
+  // (w + 4i) & 15, which takes four values per wave.
+  uint32_t dvoff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) dvoff[j] = 16u * (uint32_t)(lane ^ swz16((w + 4 * j) & 15));
 
   // Stage unit u into buffer u % NBUF.  Key rows past the tile's extent, and
   // rows of a page whose id is out of range, are zero-filled instead (never
@@ -308,15 +322,14 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   auto issue_unit = [&](int u) {
     const uint32_t ub = (uint32_t)(u % NBUF) * (UK * 1024);
     const int kl = u * UK;                         // key offset within the split
-    const int pid = __builtin_amdgcn_readfirstlane(sm_pid[kl >> 6]);
+    const int pid = __builtin_amdgcn_readfirstlane(sm_pid[pid0 + (kl >> 6)]);
     const bool pid_ok = (unsigned)pid < (unsigned)a.N;
     const uint16_t* pbase = a.pool + ((size_t)(pid_ok ? pid : 0) * PG + (kl & 63)) * D;
 #pragma unroll 8
     for (int i = 0; i < ROWS_PW; ++i) {
       const int kap = w + 4 * i;                   // key row within the unit
       if (pid_ok && k_begin + kl + kap < n_tile) {
-        dma_row16(pbase + kap * D, 16u * (uint32_t)(lane ^ swz16(kap & 15)),
-                  lds0 + ub + (uint32_t)kap * 1024u);
+        dma_row16(pbase + kap * D, dvoff[i & 3], lds0 + ub + (uint32_t)kap * 1024u);
       } else {
         *(lds_u32x4*)(sb + ub + kap * 1024 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
       }
@@ -326,7 +339,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   auto unit_ops = [&](int u) {
     if (u >= n_units) return 0;
     const int kl = u * UK;
-    const int pid = __builtin_amdgcn_readfirstlane(sm_pid[kl >> 6]);
+    const int pid = __builtin_amdgcn_readfirstlane(sm_pid[pid0 + (kl >> 6)]);
     if ((unsigned)pid >= (unsigned)a.N) return 0;
     const int valid = n_tile - (k_begin + kl);      // rows of the unit below n_tile
     if (valid >= UK) return ROWS_PW;
@@ -345,18 +358,18 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     qkb[j] = (uint32_t)(i16 * 1024 + 64 * (j ^ (swl >> 2)) + 16 * (g ^ (swl & 3)));
   // V^T: lanes 4q..4q+3 of lane group g address key rows 8g + q (+4 for the
   // second read; +32 kk for k-step kk) at dims 16 D16 + 4 (i16 & 3).  For a
-  // dim block D16: offset = trb[hi][D16 & 7] + 256 (D16 >> 3) + 32768 kk.
-  uint32_t trb[2][8];
+  // dim block D16 the offset is
+  //   trow[hi] + 32 ((D16 & 7) ^ tsw[hi]) + 256 (D16 >> 3) + 32768 kk.
+  uint32_t trow[2];
+  int tsw[2];
   {
     const int q = i16 >> 2, e4 = i16 & 3;
 #pragma unroll
     for (int hi = 0; hi < 2; ++hi) {
       const int k32 = 8 * g + q + 4 * hi;
       const int sv = swz16(k32 & 15);
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        trb[hi][j] = (uint32_t)(k32 * 1024 + 32 * (j ^ (sv >> 1)) + 16 * ((e4 >> 1) ^ (sv & 1)) +
-                                8 * (e4 & 1));
+      tsw[hi] = sv >> 1;
+      trow[hi] = (uint32_t)(k32 * 1024 + 16 * ((e4 >> 1) ^ (sv & 1)) + 8 * (e4 & 1));
     }
   }
   // P tile: this lane writes rows qrow(rb), keys qkey(kb) + 4g .. +3 and reads
@@ -402,7 +415,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     for (int kb = 0; kb < QKB; ++kb)
 #pragma unroll
       for (int rb = 0; rb < QRB; ++rb) sacc[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    constexpr int KPG = 4 / QKB;   // k-steps per operand group (4 reads per group)
+    constexpr int KPG = 2;   // k-steps per operand group
     bf16x8 kop[2][KPG][QKB];
     auto load_k = [&](bf16x8 (&dst)[KPG][QKB], int grp) {
 #pragma unroll
@@ -514,8 +527,9 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       const int d16 = w * NDT + dt;
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        const uint32_t o0 = ub + 32768u * kk + 256u * (uint32_t)(d16 >> 3) + trb[0][d16 & 7];
-        const uint32_t o1 = ub + 32768u * kk + 256u * (uint32_t)(d16 >> 3) + trb[1][d16 & 7];
+        const uint32_t base = ub + 32768u * kk + 256u * (uint32_t)(d16 >> 3);
+        const uint32_t o0 = base + trow[0] + 32u * (uint32_t)((d16 & 7) ^ tsw[0]);
+        const uint32_t o1 = base + trow[1] + 32u * (uint32_t)((d16 & 7) ^ tsw[1]);
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sb + o0));
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sb + o1));
         dst[kk] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -565,7 +579,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         for (int i = 0; i < RT / 4; ++i) {
           const int r = w + 4 * i;
           const uint16_t* src = a.q + ((size_t)b * a.R + min(row0 + r, a.R - 1)) * D;
-          dma_row16(src, 16u * (uint32_t)(lane ^ swz16(r & 15)), lds0 + qb + (uint32_t)r * 1024u);
+          dma_row16(src, dvoff[i & 3], lds0 + qb + (uint32_t)r * 1024u);
         }
       }
     }
@@ -581,8 +595,20 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int rb = 0; rb < QRB; ++rb)
 #pragma unroll
-          for (int ks = 0; ks < 16; ++ks)
-            qreg[rb][ks] = *(const lds_bf16x8*)(sb + qb + qkb[ks & 3] + 64 * (ks & 12) + 16384 * rb);
+          for (int ks = 0; ks < 16; ++ks) {
+            if (rb < 2) {
+              qreg[rb][ks] = *(const lds_bf16x8*)(sb + qb + qkb[ks & 3] + 64 * (ks & 12) + 16384 * rb);
+            } else {
+              // row blocks 2, 3 live in accumulation registers (the MFMA B
+              // operand reads them there); load them straight in so the
+              // compiler never parks them in VGPRs.  Retired by the
+              // lgkmcnt(0) of the first wait_vm_barrier below.
+              asm volatile("ds_read_b128 %0, %1 offset:%2"
+                           : "=a"(qreg[rb][ks])
+                           : "v"(lds0 + qb + qkb[ks & 3]), "i"(64 * (ks & 12) + 16384 * rb)
+                           : "memory");
+            }
+          }
         // the first wait_vm_barrier below (lgkmcnt(0) + barrier) retires these
         // reads before unit NBUF-1 is staged into the same buffer
       }
@@ -689,53 +715,51 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 }
 
 // LSE merge of the S partials of one row, computed by one wave (lane owns
-// dims 8*lane .. 8*lane+7).  The split LSEs are read in one round (lane s
-// holds split s), then the non-empty partials (bf16, normalised) are fetched
-// eight at a time with all loads in flight together.  Partials of empty
-// splits are never read (their workspace bytes may be stale).  Returns the
-// row's lse; (-inf, 0) when no split saw a key.
+// dims 8*lane .. 8*lane+7).  Lane s fetches split s's LSE while every lane
+// fetches its 16 bytes of up to 16 partials in the same round trip; the
+// weights come after.  A partial whose LSE is -inf gets weight 0 through a
+// select, so its (possibly stale) workspace bytes never reach the sum.
+// Returns the row's lse; (-inf, 0) when no split saw a key.
 __device__ __forceinline__ float merge_row(const uint16_t* __restrict__ part_o,
                                            const float* __restrict__ part_lse, int S,
                                            size_t stride_rows, size_t row, int lane, float out[8]) {
-  float acc[8];
+  constexpr int CH = 16;   // partials in flight per lane
+  const float l = (lane < S) ? part_lse[(size_t)lane * stride_rows + row] : -INFINITY;
+  uint4 v[CH];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
-  float mx = -INFINITY, wl = 0.f, total = 0.f;
-  for (int s0 = 0; s0 < S; s0 += 64) {   // S <= 64: one pass in practice
-    const float l = (s0 + lane < S) ? part_lse[(size_t)(s0 + lane) * stride_rows + row] : -INFINITY;
-    mx = fmaxf(mx, l);
-  }
+  for (int j = 0; j < CH; ++j)
+    v[j] = j < S ? *reinterpret_cast<const uint4*>(part_o + ((size_t)j * stride_rows + row) * D + lane * 8)
+                 : make_uint4(0, 0, 0, 0);
+  float mx = l;
   for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
   if (mx == -INFINITY) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) out[j] = 0.f;
     return -INFINITY;
   }
-  {
-    const float l = (lane < S) ? part_lse[(size_t)lane * stride_rows + row] : -INFINITY;
-    wl = (l == -INFINITY) ? 0.f : expf(l - mx);   // this lane's split weight
-    total = wl;
-    for (int off = 32; off >= 1; off >>= 1) total += __shfl_xor(total, off);
-  }
-  for (int s0 = 0; s0 < S; s0 += 8) {
-    uint4 v[8];
-    float ws[8];
+  const float wl = (l == -INFINITY) ? 0.f : expf(l - mx);   // this lane's split weight
+  float total = wl;
+  for (int off = 32; off >= 1; off >>= 1) total += __shfl_xor(total, off);
+  float acc[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int sj = s0 + j;
-      ws[j] = __shfl(wl, sj < S ? sj : 0);
-      ws[j] = sj < S ? ws[j] : 0.f;
-      v[j] = ws[j] > 0.f   // wave-uniform
-                 ? *reinterpret_cast<const uint4*>(part_o + ((size_t)sj * stride_rows + row) * D + lane * 8)
-                 : make_uint4(0, 0, 0, 0);
+  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+  for (int s0 = 0; s0 < S; s0 += CH) {
+    if (s0 > 0) {   // more than 16 splits: next batch
+#pragma unroll
+      for (int j = 0; j < CH; ++j)
+        v[j] = s0 + j < S
+                   ? *reinterpret_cast<const uint4*>(part_o + ((size_t)(s0 + j) * stride_rows + row) * D + lane * 8)
+                   : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < CH; ++j) {
+      const float ws = __shfl(wl, (s0 + j) & 63);
+      const bool use = s0 + j < S && ws > 0.f;
       const uint32_t wd[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        acc[2 * e] += ws[j] * bf16_to_f32(wd[e] & 0xFFFFu);
-        acc[2 * e + 1] += ws[j] * bf16_to_f32(wd[e] >> 16);
+        acc[2 * e] += use ? ws * bf16_to_f32(wd[e] & 0xFFFFu) : 0.f;
+        acc[2 * e + 1] += use ? ws * bf16_to_f32(wd[e] >> 16) : 0.f;
       }
     }
   }
