@@ -50,11 +50,14 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
-// fp32 -> bf16 bits, round to nearest even (inputs here are finite).
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+// fp32 -> bf16, round to nearest even, on the hardware converter
+// (v_cvt_pk_bf16_f32): two values per instruction, lo in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
+__device__ __forceinline__ uint16_t bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __builtin_bit_cast(float, bits16 << 16);
 }
@@ -167,26 +170,39 @@ __device__ __forceinline__ void settle_acc(f32x4& acc) { asm volatile("s_nop 7" 
 
 // Wait until at most `allowed` of this wave's vector-memory operations are
 // outstanding and its LDS writes are done, then barrier.  Memory operations
-// complete in issue order, so rounding `allowed` down is always safe.
+// complete in issue order, so rounding `allowed` down (to a multiple of 8
+// here) is always safe.  `allowed` must be wave-uniform.
 __device__ __forceinline__ void wait_vm_barrier(int allowed) {
-  if (allowed >= 32)
-    asm volatile("s_waitcnt vmcnt(32) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else if (allowed >= 16)
-    asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else if (allowed >= 8)
-    asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  switch (allowed >= 56 ? 7 : (allowed < 0 ? 0 : allowed >> 3)) {
+    case 7: asm volatile("s_waitcnt vmcnt(56) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    case 6: asm volatile("s_waitcnt vmcnt(48) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    case 5: asm volatile("s_waitcnt vmcnt(40) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(32) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(24) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+  }
 }
 
 // Logical work item of a workgroup.  Hardware deals workgroups to the 8 XCDs
-// round-robin (bid % 8); logical items are laid out in contiguous runs per
-// XCD, so the row tiles and splits that read the same pages share one L2.
-// Returns -1 for the padding workgroups of a grid rounded up to a multiple of 8.
-__device__ __forceinline__ int logical_item(int bid, int n_items) {
-  const int per = (n_items + mla::kNumXCDs - 1) / mla::kNumXCDs;
-  const int li = (bid % mla::kNumXCDs) * per + bid / mla::kNumXCDs;
-  return li < n_items ? li : -1;
+// round-robin (bid % 8); each XCD has its own L2.  A group is one (request,
+// KV split) pair, and the row tiles of a group (which read the same pages)
+// always sit in consecutive slots of one XCD.  Groups are laid out either
+//   contiguous (rr == 0): each XCD takes a run of consecutive groups, so the
+//       splits of a request share its Q tile in one L2; or
+//   round-robin (rr == 1): group g goes to XCD g % 8, so the splits of one
+//       long request land on different dies and a ragged batch spreads evenly
+//       (used when a request has several row tiles: there the per-die load,
+//       not the Q re-read, decides the time).
+// The grid is 8 * ceil(groups / 8) * row_tiles workgroups; returns -1 for the
+// padding ones.
+__device__ __forceinline__ int logical_item(int bid, int n_groups, int row_tiles, int rr) {
+  const int x = bid % mla::kNumXCDs, pos = bid / mla::kNumXCDs;
+  const int per = (n_groups + mla::kNumXCDs - 1) / mla::kNumXCDs;   // group slots per XCD
+  const int slot = pos / row_tiles;
+  const int g = rr ? slot * mla::kNumXCDs + x : x * per + slot;
+  return g < n_groups ? g * row_tiles + pos % row_tiles : -1;
 }
 
 // Verify attention over one (request b, KV split s, row tile) work item.
@@ -242,7 +258,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
   const int g = lane >> 4, i16 = lane & 15;
 
-  int id = logical_item(blockIdx.x, a.B * a.S * a.row_tiles);
+  int id = logical_item(blockIdx.x, a.B * a.S, a.row_tiles, a.row_tiles > 1);
   if (id < 0) return;
   const int rt = id % a.row_tiles;
   id /= a.row_tiles;
@@ -305,6 +321,13 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   const int k_end = min(p_end * PG, n_tile);
   const int n_units = k_end > k_begin ? (k_end - k_begin + UK - 1) / UK : 0;
 
+  if (n_units == 0 && !a.direct) {
+    // no key of this split is visible to the tile: its partial rows are the
+    // identity (lse = -inf), and the merge never reads their O
+    for (int r = tid; r < rows_here; r += kThreads)
+      a.part_lse[(size_t)s * a.B * a.R + (size_t)b * a.R + row0 + r] = -INFINITY;
+    return;
+  }
   if (!whole_row)
     for (int i = tid; i < p_end - p_begin; i += 256) sm_pid[i] = a.bt[b * a.P + p_begin + i];
   const int pid0 = whole_row ? p_begin : 0;   // sm_pid index of the split's first page
@@ -469,7 +492,9 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
           sv[kb][rb][i] = v;
         }
     }
-    if (u == 0) {   // fix every row's reference for the whole item
+    int first = __builtin_amdgcn_readfirstlane(u == 0 ? 1 : 0);
+    asm volatile("" : "+s"(first));   // opaque, so the key loop is not peeled for u == 0
+    if (first) {   // fix every row's reference for the whole item
       if (pass == 0) {
         float m[QRB];
 #pragma unroll
@@ -566,66 +591,62 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     int ops_ring[NBUF];   // DMA count per in-flight unit, indexed by u % NBUF
 #pragma unroll
     for (int j = 0; j < NBUF; ++j) ops_ring[j] = 0;
-    if (n_units > 0) {
-      issue_unit(0);
-      ops_ring[0] = unit_ops(0);
-    }
-    if constexpr (KS) {
-      if (pass == 0) {
-        // Q tile rows -> the last staging buffer (free until unit NBUF-1),
-        // swizzled like key rows so the operand reads below match the K reads
-        const uint32_t qb = (uint32_t)(NBUF - 1) * (UK * 1024);
+    int issued = 0;       // units issued so far (uniform)
+    auto issue_next = [&]() {
+      issue_unit(issued);
+      ops_ring[issued % NBUF] = unit_ops(issued);
+      ++issued;
+    };
+    // Key-split tiles stage Q through the last buffer, first, so that Q can
+    // reach the registers while unit 0 is still in flight.
+    const bool stage_q = KS && pass == 0;
+    const uint32_t qb = (uint32_t)(NBUF - 1) * (UK * 1024);
+    if (stage_q) {
 #pragma unroll
-        for (int i = 0; i < RT / 4; ++i) {
-          const int r = w + 4 * i;
-          const uint16_t* src = a.q + ((size_t)b * a.R + min(row0 + r, a.R - 1)) * D;
-          dma_row16(src, dvoff[i & 3], lds0 + qb + (uint32_t)r * 1024u);
-        }
+      for (int i = 0; i < RT / 4; ++i) {
+        const int r = w + 4 * i;
+        const uint16_t* src = a.q + ((size_t)b * a.R + min(row0 + r, a.R - 1)) * D;
+        dma_row16(src, dvoff[i & 3], lds0 + qb + (uint32_t)r * 1024u);
       }
     }
-    // The compiler counts only its own loads (Q, bounds, page ids), not the
-    // staging DMAs above.  Draining everything here, where unit 0 has to land
-    // anyway, leaves it no reason to wait on the memory counter inside the
-    // key loop, where such a wait would also stall on the prefetched units.
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-    if constexpr (KS) {
-      if (pass == 0) {
-        asm volatile("s_barrier" ::: "memory");   // every wave's Q rows landed
-        const uint32_t qb = (uint32_t)(NBUF - 1) * (UK * 1024);
+    if (n_units > 0) issue_next();
+    if (stage_q) {
+      // every wave's Q rows landed (only unit 0's DMAs may be outstanding)
+      wait_vm_barrier(__builtin_amdgcn_readfirstlane(ops_ring[0]));
 #pragma unroll
-        for (int rb = 0; rb < QRB; ++rb)
+      for (int rb = 0; rb < QRB; ++rb)
 #pragma unroll
-          for (int ks = 0; ks < 16; ++ks) {
-            if (rb < 2) {
-              qreg[rb][ks] = *(const lds_bf16x8*)(sb + qb + qkb[ks & 3] + 64 * (ks & 12) + 16384 * rb);
-            } else {
-              // row blocks 2, 3 live in accumulation registers (the MFMA B
-              // operand reads them there); load them straight in so the
-              // compiler never parks them in VGPRs.  Retired by the
-              // lgkmcnt(0) of the first wait_vm_barrier below.
-              asm volatile("ds_read_b128 %0, %1 offset:%2"
-                           : "=a"(qreg[rb][ks])
-                           : "v"(lds0 + qb + qkb[ks & 3]), "i"(64 * (ks & 12) + 16384 * rb)
-                           : "memory");
-            }
+        for (int ks = 0; ks < 16; ++ks) {
+          if (rb < 2) {
+            qreg[rb][ks] = *(const lds_bf16x8*)(sb + qb + qkb[ks & 3] + 64 * (ks & 12) + 16384 * rb);
+          } else {
+            // row blocks 2, 3 live in accumulation registers (the MFMA B
+            // operand reads them there); load them straight in so the
+            // compiler never parks them in VGPRs
+            asm volatile("ds_read_b128 %0, %1 offset:%2"
+                         : "=a"(qreg[rb][ks])
+                         : "v"(lds0 + qb + qkb[ks & 3]), "i"(64 * (ks & 12) + 16384 * rb)
+                         : "memory");
           }
-        // the first wait_vm_barrier below (lgkmcnt(0) + barrier) retires these
-        // reads before unit NBUF-1 is staged into the same buffer
-      }
+        }
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // the Q buffer is free again
+    } else {
+      // The compiler counts only its own loads (row-split Q, bounds, page
+      // ids), not the staging DMAs.  Draining everything here, where unit 0
+      // has to land anyway, leaves it no reason to wait on the memory counter
+      // inside the key loop, where such a wait would also stall on the
+      // prefetched units.
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     }
-    for (int u = 1; u < AHEAD && u < n_units; ++u) {
-      issue_unit(u);
-      ops_ring[u % NBUF] = unit_ops(u);
-    }
+    // every buffer not holding unit 0 is free: fill them
+    while (issued < n_units && issued <= AHEAD) issue_next();
     for (int u = 0; u < n_units; ++u) {
       int newer = 0;   // DMA ops issued after unit u's
 #pragma unroll
-      for (int j = 1; j < AHEAD; ++j) newer += (u + j < n_units) ? ops_ring[(u + j) % NBUF] : 0;
+      for (int j = 1; j <= AHEAD; ++j) newer += (u + j < issued) ? ops_ring[(u + j) % NBUF] : 0;
       wait_vm_barrier(__builtin_amdgcn_readfirstlane(newer));   // unit u staged; unit u-1 no longer read
-      if (u + AHEAD < n_units) {
-        issue_unit(u + AHEAD);
-        ops_ring[(u + AHEAD) % NBUF] = unit_ops(u + AHEAD);
-      }
+      // unit u-1's buffer is free: the unit AHEAD past u goes there
+      if (issued < n_units && issued <= u + AHEAD) issue_next();
       compute_unit(u, pass);
     }
     // MFMA write -> VALU write of the same accumulator (a second pass clears
@@ -669,8 +690,10 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   }
   __syncthreads();
 
-  // ---- finalize: (-inf, 0) for rows without a visible key; each wave writes
-  // its latent dims of every row, wave 0 the LSEs
+  // ---- finalize: (-inf, 0) for rows without a visible key.  The scaled bf16
+  // rows are staged in the (now idle) key buffers, swizzled by 16-byte chunk,
+  // and then leave as whole 1 KiB rows, one store instruction per row.
+  static_assert(RT * 1024 <= kBufBytes, "row staging");
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     const int row = rb * 16 + i16;
@@ -682,36 +705,44 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     }
     const bool empty = !(lr > 0.f);   // a visible key contributes P >= 1 (its max set the reference)
     const float inv = empty ? 0.f : 1.f / lr;
-    const bool store = row0 + row < a.R;
-    const size_t row_g = (size_t)b * a.R + row0 + row;
-    if (a.direct) {
-      uint16_t* dst = a.out_lat + row_g * D + 128 * w + 4 * g;
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const f32x4 v = o[dt][rb] * inv;
-        uint2 wv;
-        wv.x = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
-        wv.y = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
-        if (store) *reinterpret_cast<uint2*>(dst + 16 * dt) = wv;
-      }
-      if (store && w == 0 && g == 0)
-        a.lse[row_g] = empty ? -INFINITY : (st_m[row] + log2f(le)) * kLn2;
-    } else {
-      const size_t prow = (size_t)s * a.B * a.R + row_g;
-      if (store && w == 0 && g == 0)
-        a.part_lse[prow] = empty ? -INFINITY : (st_m[row] + log2f(le)) * kLn2;
-      if (empty || !store) continue;   // the merge never reads partials with lse = -inf
-      uint16_t* dst = a.part_o + prow * D + 128 * w + 4 * g;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const f32x4 v = o[dt][rb] * inv;
-        uint2 wv;
-        wv.x = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
-        wv.y = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
-        *reinterpret_cast<uint2*>(dst + 16 * dt) = wv;
-      }
+    for (int dt = 0; dt < NDT; ++dt) {
+      const f32x4 v = o[dt][rb] * inv;
+      const u32x2 wv = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      const int chunk = 16 * w + 2 * dt + (g >> 1);   // 16-byte chunk of dims 128 w + 16 dt + 4 g
+      *(lds_u32x2*)(sb + row * 1024 + 16 * (chunk ^ (row & 15)) + 8 * (g & 1)) = wv;
+    }
+    if (w == 0 && g == 0 && row0 + row < a.R) {
+      const size_t row_g = (size_t)b * a.R + row0 + row;
+      const float l = empty ? -INFINITY : (st_m[row] + log2f(le)) * kLn2;
+      if (a.direct) a.lse[row_g] = l;
+      else a.part_lse[(size_t)s * a.B * a.R + row_g] = l;
     }
   }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // wave w stores tile rows w, w + 4, ...; a split's empty rows are skipped
+  // (the merge never reads a partial whose lse is -inf)
+  constexpr int RPW = RT / 4;   // rows per wave
+  uint16_t* const dst0 = a.direct ? a.out_lat + ((size_t)b * a.R + row0) * D
+                                  : a.part_o + ((size_t)s * a.B * a.R + (size_t)b * a.R + row0) * D;
+  const int n_rows = min(RT, a.R - row0);
+  bool live = false;   // lane j: does row w + 4 j get stored
+  if (lane < RPW && w + 4 * lane < n_rows) {
+    float lr = 0.f;
+#pragma unroll
+    for (int k = 0; k < NSLOT; ++k) lr += st_lr[k * RT + w + 4 * lane];
+    live = a.direct || lr > 0.f;
+  }
+  const uint64_t live_mask = __ballot(live);
+  u32x4 rowv[RPW];
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const int row = w + 4 * i;
+    rowv[i] = *(const lds_u32x4*)(sb + row * 1024 + 16 * (lane ^ (row & 15)));
+  }
+#pragma unroll
+  for (int i = 0; i < RPW; ++i)
+    if ((live_mask >> i) & 1) *reinterpret_cast<u32x4*>(dst0 + (size_t)(w + 4 * i) * D + 8 * lane) = rowv[i];
 }
 
 // LSE merge of the S partials of one row, computed by one wave (lane owns
@@ -779,10 +810,10 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint16_t* __res
   float v[8];
   const float l = merge_row(part_o, part_lse, S, (size_t)rows, (size_t)row, lane, v);
   uint4 w;
-  w.x = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
-  w.y = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
-  w.z = bf16_rne(v[4]) | (bf16_rne(v[5]) << 16);
-  w.w = bf16_rne(v[6]) | (bf16_rne(v[7]) << 16);
+  w.x = pack_bf16x2(v[0], v[1]);
+  w.y = pack_bf16x2(v[2], v[3]);
+  w.z = pack_bf16x2(v[4], v[5]);
+  w.w = pack_bf16x2(v[6], v[7]);
   *reinterpret_cast<uint4*>(out_lat + (size_t)row * D + lane * 8) = w;
   if (lane == 0) lse[row] = l;
 }
@@ -812,10 +843,10 @@ __global__ __launch_bounds__(kThreads) void gated_epilogue_kernel(
       const size_t row = (size_t)rr * H + h;
       float v[8];
       const float l = merge_row(part_o, part_lse, S, rows, row, lane, v);
-      w.x = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
-      w.y = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
-      w.z = bf16_rne(v[4]) | (bf16_rne(v[5]) << 16);
-      w.w = bf16_rne(v[6]) | (bf16_rne(v[7]) << 16);
+      w.x = pack_bf16x2(v[0], v[1]);
+      w.y = pack_bf16x2(v[2], v[3]);
+      w.z = pack_bf16x2(v[4], v[5]);
+      w.w = pack_bf16x2(v[6], v[7]);
       if (out_lat) *reinterpret_cast<uint4*>(out_lat + row * D + lane * 8) = w;
       if (lane == 0) lse[row] = l;
     }
@@ -850,7 +881,7 @@ __global__ __launch_bounds__(kThreads) void gated_epilogue_kernel(
       const int d = nt * 16 + i16;
       const float x = bf16_to_f32(gate[base + d]);
       const float sg = 1.f / (1.f + expf(-x));
-      out[base + d] = (uint16_t)bf16_rne(acc[nt][i] * sg);
+      out[base + d] = bf16_bits(acc[nt][i] * sg);
     }
   }
 }
@@ -888,8 +919,8 @@ __global__ __launch_bounds__(kThreads) void absorb_q_kernel(const uint16_t* __re
     const int rr = rr0 + r;
     if (rr >= BT) break;
     uint16_t* dst = q_lat + ((size_t)rr * H + h) * D;
-    dst[tid] = (uint16_t)bf16_rne(acc0[r]);
-    dst[tid + 256] = (uint16_t)bf16_rne(acc1[r]);
+    dst[tid] = bf16_bits(acc0[r]);
+    dst[tid + 256] = bf16_bits(acc1[r]);
   }
 }
 
@@ -957,8 +988,9 @@ int run_attention(const mla_verify_params* p, const mla::Plan& pl, const mla_bf1
     a.out_lat = out_lat;
     a.lse = lse;
   }
-  const size_t items = (size_t)p->batch * pl.row_tiles * pl.splits;
-  const unsigned grid = (unsigned)((items + mla::kNumXCDs - 1) / mla::kNumXCDs * mla::kNumXCDs);
+  const size_t groups = (size_t)p->batch * pl.splits;
+  const unsigned grid =
+      (unsigned)((groups + mla::kNumXCDs - 1) / mla::kNumXCDs * mla::kNumXCDs * pl.row_tiles);
   const int mode = pl.shape.mode;
   if (mode == 0)
     hipLaunchKernelGGL((attn_kernel<0>), dim3(grid), dim3(256), kAttnSmemBytes, stream, a);
