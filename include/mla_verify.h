@@ -147,6 +147,13 @@ int mla_verify_attn(const mla_verify_params* p,
  *                                   own softmax sum; rows whose split sees no
  *                                   key are left unwritten
  *   part_lse  [S, B*T*H]      fp32  split s's natural-log LSE (-inf: no key)
+ * Partition: the folded rows of a request are processed in tiles of 32, 64
+ * or 128 rows (R <= 32, <= 64, larger); a tile sees n = ceil(L / 64) pages,
+ * L its largest token bound.  Those pages go to S' = min(S, ceil(n / m))
+ * contiguous splits, split s < S' holding pages [floor(s n / S'),
+ * floor((s+1) n / S')), with m = max(1, floor(ceil(P / S) / 2)); splits
+ * s >= S' are empty (lse = -inf).  For a batch of similar lengths S' = S; a
+ * short request in a ragged batch takes fewer splits.
  * Combining: lse = ln sum_s exp(lse_s), out = sum_s exp(lse_s - lse) part_o_s
  * (mla_verify_lse_combine).  Errors as mla_verify_attn. */
 int mla_verify_attn_partials(const mla_verify_params* p,

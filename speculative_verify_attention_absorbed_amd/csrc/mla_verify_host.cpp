@@ -63,6 +63,12 @@ Plan make_plan(const mla_verify_params* p, bool gated) {
   const int min_s = (p->max_pages_per_req + kMaxSplitPages - 1) / kMaxSplitPages;
   if (p->num_splits == 0 && s < min_s) s = min_s;
   pl.splits = s;
+  // Splits adapt to each request's own length: at least half the pages the
+  // longest possible request puts in one split.  For a batch of similar
+  // lengths this gives S splits per request; in a ragged one a short request
+  // takes fewer (each split is a workgroup with a fixed setup cost).
+  const int per_split = (p->max_pages_per_req + s - 1) / s;
+  pl.min_split_pages = per_split / 2 > 1 ? per_split / 2 : 1;
   pl.use_partials = gated || s > 1;
   const size_t total_rows = (size_t)p->batch * pl.rows;
   // partial outputs in bf16, partial LSEs in fp32

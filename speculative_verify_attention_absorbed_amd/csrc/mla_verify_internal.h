@@ -28,6 +28,7 @@ struct Plan {
   TileShape shape;
   int row_tiles;        // ceil(R / tile rows)
   int splits;           // S
+  int min_split_pages;  // m: a request of n pages takes min(S, ceil(n / m)) splits
   bool use_partials;    // results go through the partial workspace (bf16 O, fp32 LSE)
   size_t workspace_bytes;
 };

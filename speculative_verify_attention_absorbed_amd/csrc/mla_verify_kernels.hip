@@ -84,6 +84,7 @@ struct AttnArgs {
   int B, T, H, R, P, N, S, row_tiles;
   float scale_log2;        // sm_scale * log2(e)
   int direct;              // 1: write out_lat/lse, 0: write partials
+  int min_split_pages;     // a split holds at least this many pages (m)
 };
 
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
@@ -191,17 +192,20 @@ __device__ __forceinline__ void wait_vm_barrier(int allowed) {
 // always sit in consecutive slots of one XCD.  Groups are laid out either
 //   contiguous (rr == 0): each XCD takes a run of consecutive groups, so the
 //       splits of a request share its Q tile in one L2; or
-//   round-robin (rr == 1): group g goes to XCD g % 8, so the splits of one
-//       long request land on different dies and a ragged batch spreads evenly
-//       (used when a request has several row tiles: there the per-die load,
-//       not the Q re-read, decides the time).
+//   dealt (rr == 1): slot j of XCD x holds group 8 j + ((x - j) mod 8), so
+//       the splits of one request land on different dies, and split s of
+//       request b on die (b + s) mod 8 when S = 8: the first splits (never
+//       empty) rotate over the dies, and a ragged batch spreads evenly (used
+//       when a request has several row tiles: there the per-die load, not
+//       the Q re-read, decides the time).
 // The grid is 8 * ceil(groups / 8) * row_tiles workgroups; returns -1 for the
 // padding ones.
+static_assert((mla::kNumXCDs & (mla::kNumXCDs - 1)) == 0, "XCD count is a power of two");
 __device__ __forceinline__ int logical_item(int bid, int n_groups, int row_tiles, int rr) {
   const int x = bid % mla::kNumXCDs, pos = bid / mla::kNumXCDs;
   const int per = (n_groups + mla::kNumXCDs - 1) / mla::kNumXCDs;   // group slots per XCD
   const int slot = pos / row_tiles;
-  const int g = rr ? slot * mla::kNumXCDs + x : x * per + slot;
+  const int g = rr ? slot * mla::kNumXCDs + ((x - slot) & (mla::kNumXCDs - 1)) : x * per + slot;
   return g < n_groups ? g * row_tiles + pos % row_tiles : -1;
 }
 
@@ -283,19 +287,11 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   if (whole_row)
     for (int i = tid; i < a.P; i += 256) sm_pid[i] = a.bt[b * a.P + i];
 
-  // ---- Q^T of this wave's QK rows.  Row-split tiles load their own rows
-  // here (in flight while the first pages stream); key-split tiles, where
-  // every wave needs every row, stage the tile once through LDS below.
+  // ---- Q^T of this wave's QK rows, loaded in the pipeline prologue below:
+  // row-split tiles load their own rows straight into registers, next to
+  // unit 0's pages; key-split tiles, where every wave needs every row, stage
+  // the tile once through LDS.
   bf16x8 qreg[QRB][16];   // qreg[rb][ks] = Q[tile row qrow(rb)][32 ks + 8 g .. +7]
-  if constexpr (!KS) {
-#pragma unroll
-    for (int rb = 0; rb < QRB; ++rb) {
-      const int r = min(row0 + qrow(rb), a.R - 1);
-      const uint4* qp = reinterpret_cast<const uint4*>(a.q + ((size_t)b * a.R + r) * D);
-#pragma unroll
-      for (int ks = 0; ks < 16; ++ks) qreg[rb][ks] = __builtin_bit_cast(bf16x8, qp[ks * 4 + g]);
-    }
-  }
 
   int n_tile = tb;
 #pragma unroll
@@ -314,9 +310,13 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   for (int off = 32; off >= 1; off >>= 1) lmin = min(lmin, __shfl_xor(lmin, off));
   lmin = __builtin_amdgcn_readfirstlane(lmin);
 
+  // The tile's n_pg pages are cut into S' = min(S, ceil(n_pg / m)) balanced
+  // splits; splits s >= S' are empty.  A short request in a ragged batch so
+  // takes fewer, fuller splits instead of S slivers.
   const int n_pg = (n_tile + PG - 1) / PG;
-  const int p_begin = (s * n_pg) / a.S;
-  const int p_end = ((s + 1) * n_pg) / a.S;   // p_end - p_begin <= kMaxSplitPages (host check)
+  const int s_eff = min(a.S, max(1, (n_pg + a.min_split_pages - 1) / a.min_split_pages));
+  const int p_begin = s < s_eff ? (s * n_pg) / s_eff : n_pg;
+  const int p_end = s < s_eff ? ((s + 1) * n_pg) / s_eff : n_pg;   // <= kMaxSplitPages pages (host check)
   const int k_begin = p_begin * PG;
   const int k_end = min(p_end * PG, n_tile);
   const int n_units = k_end > k_begin ? (k_end - k_begin + UK - 1) / UK : 0;
@@ -588,19 +588,33 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       lround[rb] = lexact[rb] = 0.f;
     }
     jumped = false;
-    int ops_ring[NBUF];   // DMA count per in-flight unit, indexed by u % NBUF
-#pragma unroll
-    for (int j = 0; j < NBUF; ++j) ops_ring[j] = 0;
+    // DMA count per in-flight unit, 8 bits per unit u at bit 8 (u % NBUF)
+    // (a packed register, not an indexed array, which would go to scratch)
+    static_assert(NBUF <= 4 && ROWS_PW < 256, "ops ring packing");
+    uint32_t ops_ring = 0;
+    auto ring_get = [&](int v) { return (int)((ops_ring >> (8 * (v % NBUF))) & 0xFFu); };
     int issued = 0;       // units issued so far (uniform)
     auto issue_next = [&]() {
       issue_unit(issued);
-      ops_ring[issued % NBUF] = unit_ops(issued);
+      const uint32_t sh = 8u * (uint32_t)(issued % NBUF);
+      ops_ring = (ops_ring & ~(0xFFu << sh)) | ((uint32_t)unit_ops(issued) << sh);
       ++issued;
     };
     // Key-split tiles stage Q through the last buffer, first, so that Q can
     // reach the registers while unit 0 is still in flight.
     const bool stage_q = KS && pass == 0;
     const uint32_t qb = (uint32_t)(NBUF - 1) * (UK * 1024);
+    if constexpr (!KS) {
+      if (pass == 0) {
+#pragma unroll
+        for (int rb = 0; rb < QRB; ++rb) {
+          const int r = min(row0 + qrow(rb), a.R - 1);
+          const uint4* qp = reinterpret_cast<const uint4*>(a.q + ((size_t)b * a.R + r) * D);
+#pragma unroll
+          for (int ks = 0; ks < 16; ++ks) qreg[rb][ks] = __builtin_bit_cast(bf16x8, qp[ks * 4 + g]);
+        }
+      }
+    }
     if (stage_q) {
 #pragma unroll
       for (int i = 0; i < RT / 4; ++i) {
@@ -612,7 +626,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     if (n_units > 0) issue_next();
     if (stage_q) {
       // every wave's Q rows landed (only unit 0's DMAs may be outstanding)
-      wait_vm_barrier(__builtin_amdgcn_readfirstlane(ops_ring[0]));
+      wait_vm_barrier(__builtin_amdgcn_readfirstlane(ring_get(0)));
 #pragma unroll
       for (int rb = 0; rb < QRB; ++rb)
 #pragma unroll
@@ -638,15 +652,18 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       // prefetched units.
       __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     }
-    // every buffer not holding unit 0 is free: fill them
-    while (issued < n_units && issued <= AHEAD) issue_next();
+    // unit 1 now; the pipeline then deepens by one unit per step until AHEAD
+    // units are in flight (issuing them all here would hold back unit 0)
+    if (issued < n_units) issue_next();
     for (int u = 0; u < n_units; ++u) {
       int newer = 0;   // DMA ops issued after unit u's
 #pragma unroll
-      for (int j = 1; j <= AHEAD; ++j) newer += (u + j < issued) ? ops_ring[(u + j) % NBUF] : 0;
+      for (int j = 1; j <= AHEAD; ++j) newer += (u + j < issued) ? ring_get(u + j) : 0;
       wait_vm_barrier(__builtin_amdgcn_readfirstlane(newer));   // unit u staged; unit u-1 no longer read
-      // unit u-1's buffer is free: the unit AHEAD past u goes there
+      // unit u-1's buffer is free: the unit AHEAD past u goes there; while
+      // the pipeline is still filling, one more joins it
       if (issued < n_units && issued <= u + AHEAD) issue_next();
+      if (issued < n_units && issued <= u + AHEAD && u > 0) issue_next();
       compute_unit(u, pass);
     }
     // MFMA write -> VALU write of the same accumulator (a second pass clears
@@ -980,6 +997,7 @@ int run_attention(const mla_verify_params* p, const mla::Plan& pl, const mla_bf1
   a.S = pl.splits;
   a.row_tiles = pl.row_tiles;
   a.scale_log2 = p->sm_scale * kLog2e;
+  a.min_split_pages = pl.min_split_pages;
   a.direct = partials ? 0 : 1;
   if (partials) {
     a.part_o = part_o;

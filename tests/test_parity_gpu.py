@@ -253,14 +253,21 @@ def test_fp8_request_raises():
 
 
 # ------------------------------------------------ partials + combine entry points
-@pytest.mark.parametrize("cfg,splits", [(3, 4), (2, 5)])
-def test_partials_match_oracle_chunks_and_combine_matches_call(cfg, splits):
+def library_split_count(n_keys, num_splits, max_pages):
+    """The library's split rule for a request processed as one row tile (the
+    rule the header documents for mla_verify_attn_partials): its n_pg pages
+    go to S' = min(S, ceil(n_pg / m)) balanced splits, m = max(1, ceil(P / S)
+    // 2); splits s >= S' are empty."""
+    n_pg = -(-n_keys // 64)
+    m = max(1, (-(-max_pages // num_splits)) // 2)
+    return min(num_splits, max(1, -(-n_pg // m)))
+
+
+def check_partials_and_combine(x, splits):
     """mla_verify_attn_partials: split s is attention over the keys of chunk s
-    (pages [floor(s n_pg / S), floor((s+1) n_pg / S)) of the request, clipped
-    to each token's bound); mla_verify_lse_combine of those partials gives
-    the same bits as mla_verify_attn."""
-    log(f"partials + combine: config {cfg} sharp, S={splits}")
-    x = make_config(cfg, sharp=True)
+    of the library's partition (clipped to each token's bound);
+    mla_verify_lse_combine of those partials gives the same bits as
+    mla_verify_attn with the same split count."""
     q_bits = oracle_qlat_bits(x)
     d = upload(x, q_latent_bits=q_bits)
     part_o, part_lse = mv.verify_attn_partials(d["q_latent"], d["pool"], d["block_table"],
@@ -268,6 +275,7 @@ def test_partials_match_oracle_chunks_and_combine_matches_call(cfg, splits):
     out, lse = mv.verify_attn(d["q_latent"], d["pool"], d["block_table"], d["kv_bounds"],
                               x.sm_scale, num_splits=splits)
     b, t, h = x.shape
+    assert t * h <= 64, "the partition rule below is the one-row-tile case"
     comb, comb_lse = mv.verify_lse_combine(part_o, part_lse)
     sync()
     assert np.array_equal(bits_of(comb), bits_of(out).reshape(b * t * h, 512))
@@ -276,10 +284,14 @@ def test_partials_match_oracle_chunks_and_combine_matches_call(cfg, splits):
     po = f64_of(part_o).reshape(splits, b, t, h, 512)
     pl = part_lse.cpu().numpy().astype(np.float64).reshape(splits, b, t, h)
     q = oracle.bf16_to_f64(q_bits)
+    max_pages = x.block_table.shape[1]
     want_o, want_l, got_o, got_l = [], [], [], []
+    n_empty = 0
     for bi in range(b):
         c_b, n_b = oracle.request_keys(x.pool, x.block_table, x.kv_bounds, bi)
-        for s, (k0, k1) in enumerate(oracle.split_pages(n_b, splits)):
+        used = library_split_count(n_b, splits, max_pages)
+        chunks = oracle.split_pages(n_b, used) + [(n_b, n_b)] * (splits - used)
+        for s, (k0, k1) in enumerate(chunks):
             for ti in range(t):
                 L = oracle.token_bound(x.kv_bounds, bi, ti, n_b)
                 hi = min(k1, L)
@@ -287,6 +299,7 @@ def test_partials_match_oracle_chunks_and_combine_matches_call(cfg, splits):
                     o, l = oracle.attend_chunk(q[bi, ti, hh], c_b[k0:max(k0, hi)], x.sm_scale)
                     if l == -np.inf:
                         assert pl[s, bi, ti, hh] == -np.inf, (s, bi, ti, hh)
+                        n_empty += 1
                         continue
                     want_o.append(o)
                     want_l.append(l)
@@ -294,3 +307,23 @@ def test_partials_match_oracle_chunks_and_combine_matches_call(cfg, splits):
                     got_l.append(pl[s, bi, ti, hh])
     assert_close_output(np.array(got_o), np.array(want_o), "partials")
     assert np.abs(np.array(got_l) - np.array(want_l)).max() <= 1e-3
+    return n_empty
+
+
+@pytest.mark.parametrize("cfg,splits", [(3, 4), (2, 5)])
+def test_partials_match_oracle_chunks_and_combine_matches_call(cfg, splits):
+    log(f"partials + combine: config {cfg} sharp, S={splits}")
+    check_partials_and_combine(make_config(cfg, sharp=True), splits)
+
+
+def test_partials_ragged_batch_takes_fewer_splits_for_short_requests():
+    """Requests of 2 to 63 pages under S = 8 with a 64-page block-table
+    stride (m = 4): the short ones use 1, 2 or 4 splits, the rest are empty."""
+    log("partials + combine: ragged batch, S=8")
+    ctx = np.array([100, 300, 900, 2500, 4000, 64 * 63 - 5])
+    x = build_inputs(batch=6, heads=8, q_len=8, ctx=ctx, max_pages=64, pool_pages=512,
+                     seed=5, gated=False)
+    used = [library_split_count(int(c), 8, 64) for c in ctx]
+    assert used == [1, 2, 4, 8, 8, 8]
+    n_empty = check_partials_and_combine(x, 8)
+    assert n_empty >= (7 + 6 + 4) * 8 * 8
