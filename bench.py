@@ -189,6 +189,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--splits", type=int, default=None, help="force num_splits (0 = library)")
+    ap.add_argument("--tile-rows", type=int, default=0, choices=[0, 32, 64, 128],
+                    help="force rows per attention workgroup (0 = library)")
     ap.add_argument("--eager", action="store_true", help="time eager launches, not graph replay")
     ap.add_argument("--warm", action="store_true", help="one pool copy (cache-warm)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -250,8 +252,9 @@ def main():
     w_uv = up(x.w_uv)
     gate = up(x.gate)
     params = mv.VerifyParams.make(b, t, h, x.block_table.shape[1], x.pool.num_pages, x.sm_scale,
-                                  splits)
+                                  splits, tile_rows=args.tile_rows)
     s_used = mv.verify_num_splits(params, gated)
+    tile_used = mv.verify_tile_rows(params, gated)
     ws_bytes = mv.verify_workspace_size(params, gated)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     rows = b * t * h
@@ -372,7 +375,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": WORKLOAD_NAMES[args.config], "batch": b, "heads": h, "q_len": t,
-                   "num_splits": s_used, "gated": gated,
+                   "num_splits": s_used, "tile_rows": tile_used, "gated": gated,
                    "cache": "warm" if args.warm else f"cold: {n_sets} rotating pool copies",
                    "launch": mode},
         "roofline": roof,

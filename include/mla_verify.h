@@ -105,6 +105,8 @@ typedef struct mla_verify_params {
   int32_t num_splits;        /* 0 = library's choice; 1..64 = forced split-KV */
   float sm_scale;            /* softmax scale, finite and > 0                */
   int32_t kv_dtype;          /* MLA_KV_BF16 only                             */
+  int32_t tile_rows;         /* 0 = library's choice; 32, 64 or 128 = forced
+                                folded rows per attention workgroup          */
 } mla_verify_params;
 
 /* Validates `p` (pure host code, no HIP call).  MLA_OK or an error code. */
@@ -113,6 +115,11 @@ int mla_verify_check(const mla_verify_params* p);
 /* The number of KV splits S the library will use for `p` (resolves
  * num_splits == 0).  Pure host code.  Returns S >= 1, or an error code. */
 int mla_verify_num_splits(const mla_verify_params* p, int gated);
+
+/* The folded rows per attention workgroup (32, 64 or 128) the library will
+ * use for `p` (resolves tile_rows == 0).  Pure host code.  Returns the tile
+ * rows, or an error code. */
+int mla_verify_tile_rows(const mla_verify_params* p, int gated);
 
 /* Workspace bytes the call needs (0 when it needs none).  `gated` selects
  * mla_verify_attn_gated.  Pure host code.  Layout: normalised partial

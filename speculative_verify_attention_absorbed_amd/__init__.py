@@ -12,7 +12,7 @@ Entry points (same names as the C ABI, without the ``mla_`` prefix):
     verify_absorb_q(...)    -> q_latent [B,T,H,512] bf16
     verify_attn_partials(...) -> (part_o [S,B*T*H,512] bf16, part_lse [S,B*T*H] f32)
     verify_lse_combine(...) -> (out_latent [rows,512] bf16, lse [rows] f32)
-    verify_check / verify_num_splits / verify_workspace_size / status_string
+    verify_check / verify_num_splits / verify_tile_rows / verify_workspace_size / status_string
 """
 from __future__ import annotations
 
@@ -22,7 +22,8 @@ import os
 
 __all__ = [
     "MlaVerifyError", "VerifyParams", "lib_path", "load_library", "verify_check",
-    "verify_num_splits", "verify_workspace_size", "verify_attn", "verify_attn_gated",
+    "verify_num_splits", "verify_tile_rows", "verify_workspace_size", "verify_attn",
+    "verify_attn_gated",
     "verify_absorb_q", "verify_attn_partials", "verify_lse_combine", "status_string",
     "EXPORTED_SYMBOLS",
 ]
@@ -37,7 +38,7 @@ KV_BF16, KV_FP8_E4M3 = 0, 1
 LATENT, PAGE, NOPE = 512, 64, 128
 
 EXPORTED_SYMBOLS = [
-    "mla_verify_check", "mla_verify_num_splits", "mla_verify_workspace_size",
+    "mla_verify_check", "mla_verify_num_splits", "mla_verify_tile_rows", "mla_verify_workspace_size",
     "mla_verify_attn", "mla_verify_attn_partials", "mla_verify_lse_combine",
     "mla_verify_attn_gated", "mla_verify_absorb_q",
     "mla_verify_status_string",
@@ -58,14 +59,15 @@ class VerifyParams(ctypes.Structure):
         ("latent_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
         ("max_pages_per_req", ctypes.c_int32), ("num_pool_pages", ctypes.c_int32),
         ("num_splits", ctypes.c_int32), ("sm_scale", ctypes.c_float), ("kv_dtype", ctypes.c_int32),
+        ("tile_rows", ctypes.c_int32),
     ]
 
     @classmethod
     def make(cls, batch, q_len, num_heads, max_pages_per_req, num_pool_pages, sm_scale,
-             num_splits=0, latent_dim=LATENT, page_size=PAGE, kv_dtype=KV_BF16):
+             num_splits=0, latent_dim=LATENT, page_size=PAGE, kv_dtype=KV_BF16, tile_rows=0):
         return cls(int(batch), int(q_len), int(num_heads), int(latent_dim), int(page_size),
                    int(max_pages_per_req), int(num_pool_pages), int(num_splits), float(sm_scale),
-                   int(kv_dtype))
+                   int(kv_dtype), int(tile_rows))
 
 
 _LIB = None
@@ -90,6 +92,8 @@ def load_library():
     lib.mla_verify_check.restype = ctypes.c_int
     lib.mla_verify_num_splits.argtypes = [P, ctypes.c_int]
     lib.mla_verify_num_splits.restype = ctypes.c_int
+    lib.mla_verify_tile_rows.argtypes = [P, ctypes.c_int]
+    lib.mla_verify_tile_rows.restype = ctypes.c_int
     lib.mla_verify_workspace_size.argtypes = [P, ctypes.c_int, ctypes.POINTER(sz)]
     lib.mla_verify_workspace_size.restype = ctypes.c_int
     lib.mla_verify_attn.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -125,6 +129,13 @@ def verify_num_splits(params: VerifyParams, gated: bool = False) -> int:
     rc = load_library().mla_verify_num_splits(ctypes.byref(params), int(bool(gated)))
     if rc < 0:
         raise MlaVerifyError(rc, "mla_verify_num_splits")
+    return rc
+
+
+def verify_tile_rows(params: VerifyParams, gated: bool = False) -> int:
+    rc = load_library().mla_verify_tile_rows(ctypes.byref(params), int(bool(gated)))
+    if rc < 0:
+        raise MlaVerifyError(rc, "mla_verify_tile_rows")
     return rc
 
 
@@ -172,11 +183,11 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
-def _params_from(q_latent, pool, block_table, sm_scale, num_splits, kv_dtype):
+def _params_from(q_latent, pool, block_table, sm_scale, num_splits, kv_dtype, tile_rows=0):
     b, t, h, d = q_latent.shape
     return VerifyParams.make(b, t, h, block_table.shape[1], pool.shape[0], sm_scale, num_splits,
                              latent_dim=d, page_size=pool.shape[1] if pool.dim() == 3 else PAGE,
-                             kv_dtype=kv_dtype)
+                             kv_dtype=kv_dtype, tile_rows=tile_rows)
 
 
 def _workspace(params, gated, workspace, device):
@@ -193,12 +204,14 @@ def _workspace(params, gated, workspace, device):
 
 
 def verify_attn(q_latent, latent_kv_pages, block_table, kv_bounds, sm_scale, *, num_splits=0,
-                out_latent=None, lse=None, workspace=None, stream=None, kv_dtype=KV_BF16):
+                out_latent=None, lse=None, workspace=None, stream=None, kv_dtype=KV_BF16,
+                tile_rows=0):
     """``mla_verify_attn``: returns (out_latent, lse).  Outputs and workspace are
     allocated with torch when not given (allocation happens here, outside the
     library)."""
     torch = _torch()
-    params = _params_from(q_latent, latent_kv_pages, block_table, sm_scale, num_splits, kv_dtype)
+    params = _params_from(q_latent, latent_kv_pages, block_table, sm_scale, num_splits, kv_dtype,
+                          tile_rows)
     _check(verify_check(params), "mla_verify_attn")
     b, t, h, d = q_latent.shape
     bf = _bf16_types()
@@ -224,10 +237,12 @@ def verify_attn(q_latent, latent_kv_pages, block_table, kv_bounds, sm_scale, *, 
 
 def verify_attn_gated(q_latent, latent_kv_pages, block_table, kv_bounds, w_uv, gate_logits,
                       sm_scale, *, num_splits=0, out=None, lse=None, out_latent=None,
-                      want_latent=False, workspace=None, stream=None, kv_dtype=KV_BF16):
+                      want_latent=False, workspace=None, stream=None, kv_dtype=KV_BF16,
+                      tile_rows=0):
     """``mla_verify_attn_gated``: returns (out, lse, out_latent or None)."""
     torch = _torch()
-    params = _params_from(q_latent, latent_kv_pages, block_table, sm_scale, num_splits, kv_dtype)
+    params = _params_from(q_latent, latent_kv_pages, block_table, sm_scale, num_splits, kv_dtype,
+                          tile_rows)
     _check(verify_check(params), "mla_verify_attn_gated")
     b, t, h, d = q_latent.shape
     bf = _bf16_types()
@@ -259,11 +274,12 @@ def verify_attn_gated(q_latent, latent_kv_pages, block_table, kv_bounds, w_uv, g
 
 def verify_attn_partials(q_latent, latent_kv_pages, block_table, kv_bounds, sm_scale, *,
                          num_splits=0, part_o=None, part_lse=None, stream=None,
-                         kv_dtype=KV_BF16):
+                         kv_dtype=KV_BF16, tile_rows=0):
     """``mla_verify_attn_partials``: returns (part_o [S, B*T*H, 512] bf16,
     part_lse [S, B*T*H] f32) with S = verify_num_splits(params)."""
     torch = _torch()
-    params = _params_from(q_latent, latent_kv_pages, block_table, sm_scale, num_splits, kv_dtype)
+    params = _params_from(q_latent, latent_kv_pages, block_table, sm_scale, num_splits, kv_dtype,
+                          tile_rows)
     _check(verify_check(params), "mla_verify_attn_partials")
     b, t, h, d = q_latent.shape
     bf = _bf16_types()

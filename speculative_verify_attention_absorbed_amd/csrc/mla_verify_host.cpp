@@ -22,6 +22,8 @@ int check_params(const mla_verify_params* p) {
   if ((int64_t)p->batch * p->max_pages_per_req > (int64_t)1 << 30) return MLA_ERR_ARG;
   if ((int64_t)p->batch * p->q_len * p->num_heads > (int64_t)1 << 24) return MLA_ERR_SHAPE;
   if (p->num_splits < 0 || p->num_splits > MLA_VERIFY_MAX_SPLITS) return MLA_ERR_ARG;
+  if (p->tile_rows != 0 && p->tile_rows != 32 && p->tile_rows != 64 && p->tile_rows != 128)
+    return MLA_ERR_ARG;
   if (!std::isfinite(p->sm_scale) || !(p->sm_scale > 0.0f)) return MLA_ERR_ARG;
   // a forced split count must keep every split within kMaxSplitPages pages
   if (p->num_splits > 0 &&
@@ -32,30 +34,42 @@ int check_params(const mla_verify_params* p) {
   return MLA_OK;
 }
 
-TileShape choose_shape(int rows) {
-  // Up to 64 rows: one tile holds every row of a request, so each page is
-  // staged once per split; the four waves split its keys in QK.  More rows:
-  // tiles of 128 rows (each wave owns 32 rows in QK), which keeps the number
-  // of times a page is re-staged per request small.
+// Library's choice of tile (when tile_rows == 0).  Up to 32 folded rows: one
+// 32-row tile.  Up to 64: one 64-row tile stages each page once per split,
+// while two 32-row tiles stage it twice (the second read hits L2) but need
+// half the splits to fill the GPU, so every row has half as many partials to
+// write and merge; the 32-row tiles win while they still leave at least four
+// splits per tile at one workgroup per CU (few, long requests), the 64-row
+// tile otherwise.  More rows: 128-row tiles (each wave owns 32 rows in QK),
+// which keep the number of times a page is re-staged small.
+TileShape choose_shape(int rows, int batch) {
   if (rows <= 32) return TileShape{0};
-  if (rows <= 64) return TileShape{1};
+  if (rows <= 64) return (int64_t)kNumCUs / ((int64_t)batch * 2) >= 4 ? TileShape{0} : TileShape{1};
   return TileShape{2};
+}
+
+TileShape shape_for_rows(int tile_rows) {
+  return TileShape{tile_rows == 32 ? 0 : (tile_rows == 64 ? 1 : 2)};
 }
 
 Plan make_plan(const mla_verify_params* p, bool gated) {
   Plan pl{};
   pl.rows = p->q_len * p->num_heads;
-  pl.shape = choose_shape(pl.rows);
+  pl.shape = p->tile_rows != 0 ? shape_for_rows(p->tile_rows) : choose_shape(pl.rows, p->batch);
   pl.row_tiles = (pl.rows + pl.shape.tile_rows() - 1) / pl.shape.tile_rows();
   int s = p->num_splits;
   if (s == 0) {
-    // Library's choice: about one workgroup per compute unit (a workgroup
-    // holds ~150 KiB of LDS, so one fits per CU), and at least two pages per
-    // split, since every split writes a partial row tile.
+    // Library's choice: enough workgroups to give every CU one (a workgroup
+    // holds ~150 KiB of LDS, so one fits per CU; a second round of
+    // workgroups costs more than it saves), and at least one split per 16
+    // pages of the longest possible request, so that a long request in a
+    // ragged batch is not left to a single workgroup (shorter requests then
+    // take fewer splits, see min_split_pages); never more splits than pages.
     const int64_t tiles = (int64_t)p->batch * pl.row_tiles;
-    int64_t want = (kNumCUs + tiles / 2) / tiles;
-    const int64_t cap = p->max_pages_per_req / 2 > 1 ? p->max_pages_per_req / 2 : 1;
-    if (want > cap) want = cap;
+    int64_t want = kNumCUs / tiles;
+    const int64_t by_len = (p->max_pages_per_req + 15) / 16;
+    if (want < by_len) want = by_len;
+    if (want > p->max_pages_per_req) want = p->max_pages_per_req;
     if (want > MLA_VERIFY_MAX_SPLITS) want = MLA_VERIFY_MAX_SPLITS;
     s = want < 1 ? 1 : (int)want;
   }
@@ -84,6 +98,12 @@ bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u
 extern "C" {
 
 int mla_verify_check(const mla_verify_params* p) { return mla::check_params(p); }
+
+int mla_verify_tile_rows(const mla_verify_params* p, int gated) {
+  const int rc = mla::check_params(p);
+  if (rc != MLA_OK) return rc;
+  return mla::make_plan(p, gated != 0).shape.tile_rows();
+}
 
 int mla_verify_num_splits(const mla_verify_params* p, int gated) {
   const int rc = mla::check_params(p);

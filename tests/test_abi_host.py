@@ -57,6 +57,7 @@ def test_check_accepts_valid(lib):
     (dict(sm_scale=0.0), -4), (dict(sm_scale=-1.0), -4), (dict(sm_scale=float("nan")), -4),
     (dict(sm_scale=float("inf")), -4), (dict(num_splits=-1), -4), (dict(num_splits=65), -4),
     (dict(max_pages_per_req=0), -4), (dict(num_pool_pages=0), -4),
+    (dict(tile_rows=16), -4), (dict(tile_rows=96), -4), (dict(tile_rows=-1), -4),
 ])
 def test_check_rejects(lib, kw, code):
     assert mv.verify_check(good(**kw)) == code
@@ -83,11 +84,15 @@ def test_split_plan_and_workspace(lib):
     assert mv.verify_workspace_size(p4) == 4 * rows * (512 * 2 + 4)   # bf16 partials + fp32 LSEs
     # the gated path always stages partials
     assert mv.verify_workspace_size(p1, gated=True) == rows * (512 * 2 + 4)
-    # automatic choice stays within [1, max_pages/2]
+    # automatic choice: one workgroup per CU, at least one split per 16 pages
+    # of the longest request, never more splits than pages (or than 64)
     for b, t, h, pmax in [(16, 8, 8, 24), (64, 1, 64, 24), (1, 4, 8, 4), (64, 8, 64, 128),
-                          (1, 1, 1, 1)]:
-        s = mv.verify_num_splits(good(batch=b, q_len=t, num_heads=h, max_pages_per_req=pmax))
-        assert 1 <= s <= max(1, pmax // 2)
+                          (1, 1, 1, 1), (512, 8, 64, 24), (2, 16, 128, 2000)]:
+        p = good(batch=b, q_len=t, num_heads=h, max_pages_per_req=pmax)
+        s = mv.verify_num_splits(p)
+        tiles = b * -(-(t * h) // mv.verify_tile_rows(p))
+        want = max(256 // tiles, -(-pmax // 16), 1)
+        assert s == min(want, pmax, 64), (b, t, h, pmax, s)
 
 
 def test_status_strings(lib):
@@ -129,3 +134,18 @@ def test_entry_points_validate_before_any_hip_call(lib):
     # bad params take precedence over everything else
     assert lib.mla_verify_attn(ctypes.byref(good(latent_dim=576)), z, *args[1:], z, 0, z) == -2
     assert lib.mla_verify_attn(None, *args, z, 0, z) == -1
+
+
+def test_tile_rows_forced_and_resolved(lib):
+    # forced tiles are honoured for any head fold; 0 resolves to one of 32/64/128
+    for t in (32, 64, 128):
+        assert mv.verify_tile_rows(good(tile_rows=t)) == t
+        assert mv.verify_tile_rows(good(q_len=1, num_heads=4, tile_rows=t)) == t
+    assert mv.verify_tile_rows(good()) in (32, 64, 128)
+    assert mv.verify_tile_rows(good(q_len=16, num_heads=128)) in (32, 64, 128)
+    assert lib.mla_verify_tile_rows(ctypes.byref(good(tile_rows=48)), 0) == -4
+    assert lib.mla_verify_tile_rows(None, 0) == -1
+    # the workspace follows the split count only, whatever the tile
+    for t in (32, 64, 128):
+        assert mv.verify_workspace_size(good(num_splits=4, tile_rows=t)) == \
+            4 * 16 * 8 * 8 * (512 * 2 + 4)

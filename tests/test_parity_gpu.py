@@ -24,16 +24,16 @@ def oracle_qlat_bits(x):
     return round_bf16(oracle.absorb_query(x.q_nope, x.w_uk))
 
 
-def run_latent(x, d, num_splits=None):
+def run_latent(x, d, num_splits=None, tile_rows=0):
     s = x.num_splits if num_splits is None else num_splits
     out, lse = mv.verify_attn(d["q_latent"], d["pool"], d["block_table"], d["kv_bounds"],
-                              x.sm_scale, num_splits=s)
+                              x.sm_scale, num_splits=s, tile_rows=tile_rows)
     sync()
     return f64_of(out), lse.cpu().numpy().astype(np.float64), out
 
 
-def check_latent(x, d, q_bits, num_splits=None, what=""):
-    got, lse, _ = run_latent(x, d, num_splits)
+def check_latent(x, d, q_bits, num_splits=None, what="", tile_rows=0):
+    got, lse, _ = run_latent(x, d, num_splits, tile_rows)
     want, want_lse = oracle.verify_attention_latent(q_bits, x.pool, x.block_table, x.kv_bounds,
                                                     x.sm_scale)
     assert_lse(lse, want_lse, f"{what} lse")
@@ -83,6 +83,18 @@ def test_latent_parity_config5_full():
     check_latent(x, d, q_bits, what="cfg5")
 
 
+@pytest.mark.parametrize("tile", [32, 64, 128])
+@pytest.mark.parametrize("cfg,splits", [(3, 4), (2, 8), (4, 2)])
+def test_forced_tiles_on_workloads(cfg, tile, splits):
+    """Every tile shape on the 8-head workloads (40 or 64 folded rows: one
+    partial tile of 128, one or two of 64, two of 32), against the oracle."""
+    log(f"forced tile: config {cfg} (sharp), tile {tile}, S={splits}")
+    x = make_config(cfg, sharp=True)
+    q_bits = oracle_qlat_bits(x)
+    d = upload(x, q_latent_bits=q_bits)
+    check_latent(x, d, q_bits, num_splits=splits, tile_rows=tile, what=f"tile{tile}")
+
+
 @pytest.mark.parametrize("splits", [1, 2, 3, 4, 7, 8, 16])
 def test_split_invariance(splits):
     log(f"split invariance: config 3 (sharp), S={splits}")
@@ -104,7 +116,9 @@ def test_fold_shapes(heads, q_len):
                      latent_q=True, q_scale=1536.0)
     d = upload(x)
     for s in (1, 3):
-        check_latent(x, d, x.q_latent, num_splits=s, what=f"H{heads}T{q_len}S{s}")
+        for tile in (0, 32, 64, 128):
+            check_latent(x, d, x.q_latent, num_splits=s, tile_rows=tile,
+                         what=f"H{heads}T{q_len}S{s}tile{tile}")
 
 
 def test_random_bounds_zero_rows_and_empty_requests():
@@ -121,6 +135,8 @@ def test_random_bounds_zero_rows_and_empty_requests():
     d = upload(x)
     for s in (0, 1, 2, 5):
         check_latent(x, d, x.q_latent, num_splits=s, what=f"S{s}")
+    for tile in (32, 128):
+        check_latent(x, d, x.q_latent, num_splits=2, tile_rows=tile, what=f"S2 tile{tile}")
     # bounds beyond max_pages*64 are clamped to it
     big = bounds.copy()
     big[3, 0] = 10_000_000
@@ -196,11 +212,11 @@ def test_nan_pool_outside_visible_keys_is_ignored():
 
 
 # ------------------------------------------------------------------ gated epilogue
-def check_gated(x, d, q_bits, num_splits=None, requests=None, what=""):
+def check_gated(x, d, q_bits, num_splits=None, requests=None, what="", tile_rows=0):
     s = x.num_splits if num_splits is None else num_splits
     out, lse, lat = mv.verify_attn_gated(d["q_latent"], d["pool"], d["block_table"],
                                          d["kv_bounds"], d["w_uv"], d["gate"], x.sm_scale,
-                                         num_splits=s, want_latent=True)
+                                         num_splits=s, want_latent=True, tile_rows=tile_rows)
     sync()
     o_lat, want_lse = oracle.verify_attention_latent(q_bits, x.pool, x.block_table, x.kv_bounds,
                                                      x.sm_scale)
@@ -212,13 +228,14 @@ def check_gated(x, d, q_bits, num_splits=None, requests=None, what=""):
     assert_close_output(f64_of(lat), o_lat, f"{what} gated out_latent")
 
 
-@pytest.mark.parametrize("cfg,splits", [(1, 1), (1, 2), (3, 4), (5, 8)])
-def test_gated_parity(cfg, splits):
-    log(f"gated parity: config {cfg}, S={splits}")
+@pytest.mark.parametrize("cfg,splits,tile", [(1, 1, 0), (1, 2, 0), (3, 4, 0), (5, 8, 0),
+                                            (1, 2, 128), (3, 4, 32), (5, 0, 0), (5, 8, 64)])
+def test_gated_parity(cfg, splits, tile):
+    log(f"gated parity: config {cfg}, S={splits}, tile {tile}")
     x = make_config(cfg, sharp=(cfg != 5))
     q_bits = oracle_qlat_bits(x)
     d = upload(x, q_latent_bits=q_bits)
-    check_gated(x, d, q_bits, num_splits=splits, what=f"cfg{cfg}")
+    check_gated(x, d, q_bits, num_splits=splits, what=f"cfg{cfg}", tile_rows=tile)
 
 
 # ------------------------------------------------------------------ end to end
@@ -254,66 +271,73 @@ def test_fp8_request_raises():
 
 # ------------------------------------------------ partials + combine entry points
 def library_split_count(n_keys, num_splits, max_pages):
-    """The library's split rule for a request processed as one row tile (the
-    rule the header documents for mla_verify_attn_partials): its n_pg pages
-    go to S' = min(S, ceil(n_pg / m)) balanced splits, m = max(1, ceil(P / S)
-    // 2); splits s >= S' are empty."""
+    """The library's split rule for one row tile (the rule the header documents
+    for mla_verify_attn_partials): the n_pg pages up to the tile's largest
+    bound go to S' = min(S, ceil(n_pg / m)) balanced splits, m = max(1,
+    ceil(P / S) // 2); splits s >= S' are empty."""
     n_pg = -(-n_keys // 64)
     m = max(1, (-(-max_pages // num_splits)) // 2)
     return min(num_splits, max(1, -(-n_pg // m)))
 
 
-def check_partials_and_combine(x, splits):
-    """mla_verify_attn_partials: split s is attention over the keys of chunk s
-    of the library's partition (clipped to each token's bound);
+def check_partials_and_combine(x, splits, tile_rows=0):
+    """mla_verify_attn_partials: split s of a row is attention over the keys of
+    chunk s of its row tile's partition (clipped to the row's token bound);
     mla_verify_lse_combine of those partials gives the same bits as
-    mla_verify_attn with the same split count."""
+    mla_verify_attn with the same split count and tile."""
     q_bits = oracle_qlat_bits(x)
     d = upload(x, q_latent_bits=q_bits)
     part_o, part_lse = mv.verify_attn_partials(d["q_latent"], d["pool"], d["block_table"],
-                                               d["kv_bounds"], x.sm_scale, num_splits=splits)
+                                               d["kv_bounds"], x.sm_scale, num_splits=splits,
+                                               tile_rows=tile_rows)
     out, lse = mv.verify_attn(d["q_latent"], d["pool"], d["block_table"], d["kv_bounds"],
-                              x.sm_scale, num_splits=splits)
+                              x.sm_scale, num_splits=splits, tile_rows=tile_rows)
     b, t, h = x.shape
-    assert t * h <= 64, "the partition rule below is the one-row-tile case"
     comb, comb_lse = mv.verify_lse_combine(part_o, part_lse)
     sync()
     assert np.array_equal(bits_of(comb), bits_of(out).reshape(b * t * h, 512))
     assert np.array_equal(comb_lse.cpu().numpy(), lse.cpu().numpy().reshape(-1))
 
-    po = f64_of(part_o).reshape(splits, b, t, h, 512)
-    pl = part_lse.cpu().numpy().astype(np.float64).reshape(splits, b, t, h)
-    q = oracle.bf16_to_f64(q_bits)
+    params = mv.VerifyParams.make(b, t, h, x.block_table.shape[1], x.pool.num_pages, x.sm_scale,
+                                  splits, tile_rows=tile_rows)
+    tile = mv.verify_tile_rows(params)
+    po = f64_of(part_o).reshape(splits, b, t * h, 512)
+    pl = part_lse.cpu().numpy().astype(np.float64).reshape(splits, b, t * h)
+    q = oracle.bf16_to_f64(q_bits).reshape(b, t * h, 512)
     max_pages = x.block_table.shape[1]
     want_o, want_l, got_o, got_l = [], [], [], []
     n_empty = 0
     for bi in range(b):
         c_b, n_b = oracle.request_keys(x.pool, x.block_table, x.kv_bounds, bi)
-        used = library_split_count(n_b, splits, max_pages)
-        chunks = oracle.split_pages(n_b, used) + [(n_b, n_b)] * (splits - used)
-        for s, (k0, k1) in enumerate(chunks):
-            for ti in range(t):
-                L = oracle.token_bound(x.kv_bounds, bi, ti, n_b)
-                hi = min(k1, L)
-                for hh in range(h):
-                    o, l = oracle.attend_chunk(q[bi, ti, hh], c_b[k0:max(k0, hi)], x.sm_scale)
+        for r0 in range(0, t * h, tile):
+            rows = range(r0, min(r0 + tile, t * h))
+            # the tile sees the keys up to its own largest bound
+            n_tile = max(oracle.token_bound(x.kv_bounds, bi, r // h, n_b) for r in rows)
+            used = library_split_count(n_tile, splits, max_pages)
+            chunks = oracle.split_pages(n_tile, used) + [(n_tile, n_tile)] * (splits - used)
+            for s, (k0, k1) in enumerate(chunks):
+                for r in rows:
+                    L = oracle.token_bound(x.kv_bounds, bi, r // h, n_b)
+                    hi = min(k1, L)
+                    o, l = oracle.attend_chunk(q[bi, r], c_b[k0:max(k0, hi)], x.sm_scale)
                     if l == -np.inf:
-                        assert pl[s, bi, ti, hh] == -np.inf, (s, bi, ti, hh)
+                        assert pl[s, bi, r] == -np.inf, (s, bi, r)
                         n_empty += 1
                         continue
                     want_o.append(o)
                     want_l.append(l)
-                    got_o.append(po[s, bi, ti, hh])
-                    got_l.append(pl[s, bi, ti, hh])
+                    got_o.append(po[s, bi, r])
+                    got_l.append(pl[s, bi, r])
     assert_close_output(np.array(got_o), np.array(want_o), "partials")
     assert np.abs(np.array(got_l) - np.array(want_l)).max() <= 1e-3
     return n_empty
 
 
-@pytest.mark.parametrize("cfg,splits", [(3, 4), (2, 5)])
-def test_partials_match_oracle_chunks_and_combine_matches_call(cfg, splits):
-    log(f"partials + combine: config {cfg} sharp, S={splits}")
-    check_partials_and_combine(make_config(cfg, sharp=True), splits)
+@pytest.mark.parametrize("cfg,splits,tile", [(3, 4, 0), (2, 5, 0), (2, 5, 64), (3, 3, 128),
+                                            (1, 4, 0)])
+def test_partials_match_oracle_chunks_and_combine_matches_call(cfg, splits, tile):
+    log(f"partials + combine: config {cfg} sharp, S={splits}, tile {tile}")
+    check_partials_and_combine(make_config(cfg, sharp=True), splits, tile)
 
 
 def test_partials_ragged_batch_takes_fewer_splits_for_short_requests():
@@ -325,5 +349,5 @@ def test_partials_ragged_batch_takes_fewer_splits_for_short_requests():
                      seed=5, gated=False)
     used = [library_split_count(int(c), 8, 64) for c in ctx]
     assert used == [1, 2, 4, 8, 8, 8]
-    n_empty = check_partials_and_combine(x, 8)
+    n_empty = check_partials_and_combine(x, 8, tile_rows=64)
     assert n_empty >= (7 + 6 + 4) * 8 * 8

@@ -59,7 +59,7 @@ class ConfigSpec:
 
 
 CONFIGS = {
-    1: ConfigSpec(1, 8, 4, 4, 4, "fixed256", 1, True),
+    1: ConfigSpec(1, 8, 4, 4, 4, "fixed256", 0, True),
     2: ConfigSpec(16, 8, 8, 4096, 24, "uniform", 0, False),
     3: ConfigSpec(32, 8, 5, 4096, 24, "uniform", 4, False),
     4: ConfigSpec(64, 64, 1, 4096, 24, "uniform", 0, False),
