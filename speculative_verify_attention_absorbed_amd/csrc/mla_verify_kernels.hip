@@ -20,8 +20,9 @@
 //                        normalised fp32 partials + partial lse (split-KV).
 //   combine_kernel       LSE merge of the S partials of every row (rows with
 //                        no visible key in any split give (-inf, 0)).
-//   gated_epilogue_kernel  per head: LSE merge, then W_UV (512 -> 128) on
-//                        MFMA and the sigmoid gate; optional o_lat output.
+//   gated_epilogue_kernel  per (head, 16 rows): LSE merge reading only the
+//                        partials with a nonzero weight, then W_UV (512 -> 128)
+//                        on MFMA and the sigmoid gate; optional o_lat output.
 //   absorb_q_kernel      q_latent = W_UK[h]^T q_nope, fp32 accumulate, bf16.
 #include <hip/hip_runtime.h>
 
@@ -835,70 +836,140 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint16_t* __res
   if (lane == 0) lse[row] = l;
 }
 
-// One workgroup per (head h, tile of 64 (b, t) rows).  Phase 1: each wave
-// merges 16 rows' partials and leaves o_lat (bf16) in LDS.  Phase 2: each
-// wave computes out[16 rows][128] = o_lat[16][512] . W_UV[h]^T on MFMA and
-// applies sigmoid(gate).
-__global__ __launch_bounds__(kThreads) void gated_epilogue_kernel(
+// Gated epilogue: one workgroup per (head h, 16 (b, t) rows).
+//   merge   wave w owns tile rows w, w + 4, w + 8, w + 12 and merges RB of
+//           them at a time: one round trip fetches the S LSEs of the RB rows
+//           (LPR = 64 / RB lanes per row, one split per lane), the weights
+//           exp(lse_s - max) follow, and a second round trip fetches only the
+//           partials with a nonzero weight (at most 16 in flight per lane);
+//           the bf16 o_lat rows go to an LDS tile, lse and the optional
+//           out_latent to memory.  Rows with no visible key give (-inf, 0).
+//   W_UV    wave w computes out dims 32 w .. +31 of all 16 rows on MFMA
+//           (A = o_lat tile from LDS, B = W_UV[h] rows straight from memory),
+//           then multiplies by sigmoid(gate).
+template <int RB>
+__global__ __launch_bounds__(kThreads, 3) void gated_epilogue_kernel(
     const uint16_t* __restrict__ part_o, const float* __restrict__ part_lse,
     const uint16_t* __restrict__ w_uv, const uint16_t* __restrict__ gate,
-    uint16_t* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ out_lat,
+    uint16_t* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ out_latent,
     int BT, int H, int S) {
-  extern __shared__ uint4 lds4[];   // 64 rows x 64 chunks (bf16 o_lat) = 64 KiB
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int LPR = 64 / RB;   // lanes per row for the LSEs: S <= LPR
+  constexpr int CHK = 16 / RB;   // partial loads in flight per row (16 per lane: 3 workgroups fit a CU)
+  __shared__ uint4 tile[16 * 64];   // 16 rows x 64 chunks of 16 bytes, chunk c of row r at r*64 + (c ^ (r & 15))
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, i16 = lane & 15;
   const int h = blockIdx.x % H;
-  const int tile = blockIdx.x / H;
-  const int rr0 = tile * 64;
+  const int rr0 = (blockIdx.x / H) * 16;
   const size_t rows = (size_t)BT * H;
 
-  for (int r = 0; r < 16; ++r) {
-    const int lr = wave * 16 + r;
-    const int rr = rr0 + lr;           // (b, t) row index = b*T + t
-    uint4 w = make_uint4(0, 0, 0, 0);
-    if (rr < BT) {
-      const size_t row = (size_t)rr * H + h;
-      float v[8];
-      const float l = merge_row(part_o, part_lse, S, rows, row, lane, v);
-      w.x = pack_bf16x2(v[0], v[1]);
-      w.y = pack_bf16x2(v[2], v[3]);
-      w.z = pack_bf16x2(v[4], v[5]);
-      w.w = pack_bf16x2(v[6], v[7]);
-      if (out_lat) *reinterpret_cast<uint4*>(out_lat + row * D + lane * 8) = w;
-      if (lane == 0) lse[row] = l;
+  // gate values of this lane's outputs: C[row 4g + i][dim 32 wave + 16 nt + i16]
+  float gv[2][4];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = rr0 + 4 * g + i;
+      gv[nt][i] = rr < BT ? bf16_to_f32(gate[((size_t)rr * H + h) * DV + 32 * wave + 16 * nt + i16]) : 0.f;
     }
-    lds4[swz(lr, lane)] = w;
+
+  const int qq = lane / LPR, j = lane % LPR;   // (row of the batch, split) of this lane's LSE
+#pragma unroll 1
+  for (int q0 = 0; q0 < 4; q0 += RB) {
+    // ---- LSEs and weights of rows w + 4 (q0 + qq)
+    const int lr_l = wave + 4 * (q0 + qq);
+    const int rr_l = rr0 + lr_l;
+    const size_t row_l = (size_t)rr_l * H + h;
+    const float l = (rr_l < BT && j < S) ? part_lse[(size_t)j * rows + row_l] : -INFINITY;
+    float mx = l;
+#pragma unroll
+    for (int off = LPR / 2; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    const float wl = (l == -INFINITY) ? 0.f : expf(l - mx);
+    float total = wl;
+#pragma unroll
+    for (int off = LPR / 2; off >= 1; off >>= 1) total += __shfl_xor(total, off);
+    // ---- weighted sum of the partials with a nonzero weight
+    float acc[RB][8];
+#pragma unroll
+    for (int q = 0; q < RB; ++q)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[q][e] = 0.f;
+    for (int c0 = 0; c0 < S; c0 += CHK) {
+      auto weight = [&](int q, int k) {   // weight of split c0 + k for batch row q
+        const int jj = c0 + k;
+        return jj < S ? __shfl(wl, q * LPR + (jj & (LPR - 1))) : 0.f;
+      };
+      uint4 v[RB][CHK];
+#pragma unroll
+      for (int q = 0; q < RB; ++q) {
+        const size_t row = (size_t)(rr0 + wave + 4 * (q0 + q)) * H + h;
+#pragma unroll
+        for (int k = 0; k < CHK; ++k) {
+          v[q][k] = make_uint4(0, 0, 0, 0);
+          if (weight(q, k) > 0.f)   // wave-uniform: a split the row saw no key of is never read
+            v[q][k] = *reinterpret_cast<const uint4*>(part_o + ((size_t)(c0 + k) * rows + row) * D + lane * 8);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < RB; ++q)
+#pragma unroll
+        for (int k = 0; k < CHK; ++k) {
+          const float ws = weight(q, k);
+          const uint32_t wd[4] = {v[q][k].x, v[q][k].y, v[q][k].z, v[q][k].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[q][2 * e] += ws * bf16_to_f32(wd[e] & 0xFFFFu);
+            acc[q][2 * e + 1] += ws * bf16_to_f32(wd[e] >> 16);
+          }
+        }
+    }
+    // ---- rows out: LDS tile (bf16), lse, optional out_latent
+#pragma unroll
+    for (int q = 0; q < RB; ++q) {
+      const int lr = wave + 4 * (q0 + q);
+      const int rr = rr0 + lr;
+      const float tq = __shfl(total, q * LPR);
+      const float mq = __shfl(mx, q * LPR);
+      uint4 wv = make_uint4(0, 0, 0, 0);
+      if (rr < BT && tq > 0.f) {
+        const float inv = 1.f / tq;
+        wv.x = pack_bf16x2(acc[q][0] * inv, acc[q][1] * inv);
+        wv.y = pack_bf16x2(acc[q][2] * inv, acc[q][3] * inv);
+        wv.z = pack_bf16x2(acc[q][4] * inv, acc[q][5] * inv);
+        wv.w = pack_bf16x2(acc[q][6] * inv, acc[q][7] * inv);
+      }
+      tile[lr * 64 + (lane ^ (lr & 15))] = wv;
+      if (rr < BT) {
+        const size_t row = (size_t)rr * H + h;
+        if (out_latent) *reinterpret_cast<uint4*>(out_latent + row * D + lane * 8) = wv;
+        if (lane == 0) lse[row] = tq > 0.f ? mq + logf(tq) : -INFINITY;
+      }
+    }
   }
   __syncthreads();
 
-  // out^T[d][row] would need W as A; instead C[row][d] = A[row][c] B[c][d]
-  const int lr = wave * 16 + i16;      // A row owned by this lane
-  f32x4 acc[8];
-#pragma unroll
-  for (int nt = 0; nt < 8; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // ---- out[16 rows][32 dims of this wave] = o_lat[16][512] . W_UV[h][dims][512]^T
+  f32x4 acc2[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
   const uint16_t* wh = w_uv + (size_t)h * DV * D;
 #pragma unroll 4
   for (int ks = 0; ks < 16; ++ks) {
-    const bf16x8 av = __builtin_bit_cast(bf16x8, lds4[swz(lr, ks * 4 + g)]);
+    const bf16x8 av = __builtin_bit_cast(bf16x8, tile[i16 * 64 + ((4 * ks + g) ^ i16)]);
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      const int d = nt * 16 + i16;
+    for (int nt = 0; nt < 2; ++nt) {
+      const int d = 32 * wave + 16 * nt + i16;
       const uint4 bv = *reinterpret_cast<const uint4*>(wh + (size_t)d * D + ks * 32 + 8 * g);
-      acc[nt] = mfma16(av, __builtin_bit_cast(bf16x8, bv), acc[nt]);
+      acc2[nt] = mfma16(av, __builtin_bit_cast(bf16x8, bv), acc2[nt]);
     }
   }
-  // acc[nt][i] = C[row wave*16 + 4g + i][d = nt*16 + i16]
+  // acc2[nt][i] = C[row 4g + i][dim 32 wave + 16 nt + i16]
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int rr = rr0 + wave * 16 + 4 * g + i;
+    const int rr = rr0 + 4 * g + i;
     if (rr >= BT) continue;
     const size_t base = ((size_t)rr * H + h) * DV;
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      const int d = nt * 16 + i16;
-      const float x = bf16_to_f32(gate[base + d]);
-      const float sg = 1.f / (1.f + expf(-x));
-      out[base + d] = bf16_bits(acc[nt][i] * sg);
+    for (int nt = 0; nt < 2; ++nt) {
+      const float sg = 1.f / (1.f + expf(-gv[nt][i]));
+      out[base + 32 * wave + 16 * nt + i16] = bf16_bits(acc2[nt][i] * sg);
     }
   }
 }
@@ -962,8 +1033,6 @@ int ensure_device() {
       for (const void* f : attn)
         fail |= hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kAttnSmemBytes) !=
                 hipSuccess;
-      fail |= hipFuncSetAttribute(reinterpret_cast<const void*>(gated_epilogue_kernel),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, 64 * 1024) != hipSuccess;
       if (fail)
         return MLA_ERR_HIP;
     }
@@ -1116,10 +1185,17 @@ int mla_verify_attn_gated(const mla_verify_params* p, const mla_bf16* q_latent,
   rc = run_attention(p, pl, q_latent, latent_kv_pages, block_table, kv_bounds, nullptr, nullptr, true,
                      part_o, part_lse, st);
   if (rc != MLA_OK) return rc;
-  const unsigned grid = (unsigned)(((bt_rows + 63) / 64) * p->num_heads);
-  hipLaunchKernelGGL(gated_epilogue_kernel, dim3(grid), dim3(kThreads), 64 * 1024, st, part_o,
-                     part_lse, w_uv, gate_logits, out, lse, out_latent, bt_rows, p->num_heads,
-                     pl.splits);
+  const unsigned grid = (unsigned)(((bt_rows + 15) / 16) * p->num_heads);
+  const int S = pl.splits;
+  if (S <= 8)
+    hipLaunchKernelGGL((gated_epilogue_kernel<4>), dim3(grid), dim3(kThreads), 0, st, part_o, part_lse,
+                       w_uv, gate_logits, out, lse, out_latent, bt_rows, p->num_heads, S);
+  else if (S <= 16)
+    hipLaunchKernelGGL((gated_epilogue_kernel<2>), dim3(grid), dim3(kThreads), 0, st, part_o, part_lse,
+                       w_uv, gate_logits, out, lse, out_latent, bt_rows, p->num_heads, S);
+  else
+    hipLaunchKernelGGL((gated_epilogue_kernel<1>), dim3(grid), dim3(kThreads), 0, st, part_o, part_lse,
+                       w_uv, gate_logits, out, lse, out_latent, bt_rows, p->num_heads, S);
   return launch_status();
 }
 
