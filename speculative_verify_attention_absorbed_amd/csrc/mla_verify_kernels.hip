@@ -402,7 +402,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 
   f32x4 o[NDT][NRB];   // O^T: o[dt][rb][i] = O[row 16 rb + i16][dim 128 w + 16 dt + 4 g + i]
   float mref[QRB];     // reference max of this lane's QK rows (log2 domain)
-  float mtrue[QRB];    // lane's running max of its own scores
+  float mtrue[QRB];    // lane's running max of its own raw scores
   float lround[QRB];   // lane share of sum of bf16(P): the weights PV applies
   float lexact[QRB];   // lane share of sum of P in fp32: the LSE
   float mpreset[QRB];
@@ -478,24 +478,29 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       else
         asm volatile("s_nop 7\n\ts_nop 4" : "+v"(sf[0]), "+v"(sf[1]));
     }
-    // ---- masked scores in the log2 domain
+    // ---- raw scores; keys a row does not see become -inf.  A unit every
+    // valid row of the wave sees in full (all but the last of a split, as a
+    // rule) skips the masking: a wave-uniform test.
     float sv[QKB][QRB][4];
 #pragma unroll
-    for (int kb = 0; kb < QKB; ++kb) {
-      const int key = ukey0 + qkey(kb) + 4 * g;
-      const bool full = key + 4 <= lmin;   // every valid row sees these 4 keys
+    for (int kb = 0; kb < QKB; ++kb)
 #pragma unroll
       for (int rb = 0; rb < QRB; ++rb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = sacc[kb][rb][i] * a.scale_log2;
-          if (!full) v = (key + i) < L[rb] ? v : -INFINITY;
-          sv[kb][rb][i] = v;
-        }
+        for (int i = 0; i < 4; ++i) sv[kb][rb][i] = sacc[kb][rb][i];
+    if (!(ukey0 + UK <= lmin)) {
+#pragma unroll
+      for (int kb = 0; kb < QKB; ++kb) {
+        const int key = ukey0 + qkey(kb) + 4 * g;
+#pragma unroll
+        for (int rb = 0; rb < QRB; ++rb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sv[kb][rb][i] = (key + i) < L[rb] ? sv[kb][rb][i] : -INFINITY;
+      }
     }
     int first = __builtin_amdgcn_readfirstlane(u == 0 ? 1 : 0);
     asm volatile("" : "+s"(first));   // opaque, so the key loop is not peeled for u == 0
-    if (first) {   // fix every row's reference for the whole item
+    if (first) {   // fix every row's reference for the whole item (log2 domain)
       if (pass == 0) {
         float m[QRB];
 #pragma unroll
@@ -507,36 +512,39 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
             for (int i = 0; i < 4; ++i) m[rb] = fmaxf(m[rb], sv[kb][rb][i]);
         }
         row_reduce_max(m);
+        // the scale is positive, so max(s) * scale == max(s * scale)
 #pragma unroll
-        for (int rb = 0; rb < QRB; ++rb) mref[rb] = m[rb];
+        for (int rb = 0; rb < QRB; ++rb) mref[rb] = m[rb] * a.scale_log2;
       } else {
 #pragma unroll
         for (int rb = 0; rb < QRB; ++rb) mref[rb] = mpreset[rb];
       }
     }
-    // ---- P = 2^(s - ref) in bf16 into the P tile; lane sums and maxima
+    // ---- P = 2^(s * scale - ref) in bf16 into the P tile; lane sums and
+    // raw maxima.  sum bf16(P) (the weights PV applies) comes from the packed
+    // pairs with one dot product each; sum P in fp32 (the LSE) directly.
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2v;
+    const bf16x2v ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int rb = 0; rb < QRB; ++rb) {
       const float mu = (mref[rb] == -INFINITY) ? 0.f : mref[rb];   // no visible key: P = 0
       float sr = 0.f, se = 0.f, mt = mtrue[rb];
 #pragma unroll
       for (int kb = 0; kb < QKB; ++kb) {
-        __bf16 pv[4];
+        float p[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           mt = fmaxf(mt, sv[kb][rb][i]);
-          const float p = __builtin_amdgcn_exp2f(sv[kb][rb][i] - mu);   // v_exp_f32; -inf -> 0
-          pv[i] = (__bf16)p;
-          sr += (float)pv[i];
-          se += p;
+          p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[kb][rb][i], a.scale_log2, -mu));   // -inf -> 0
         }
-        const u32x2 pw = {
-            (uint32_t)__builtin_bit_cast(uint16_t, pv[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, pv[1]) << 16),
-            (uint32_t)__builtin_bit_cast(uint16_t, pv[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, pv[3]) << 16)};
-        *(lds_u32x2*)(sp + qrow(rb) * PPITCH + 2 * (qkey(kb) + 4 * g)) = pw;
+        const uint32_t lo = pack_bf16x2(p[0], p[1]), hi = pack_bf16x2(p[2], p[3]);
+        sr = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, lo), ones, sr, false);
+        sr = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, hi), ones, sr, false);
+        se += (p[0] + p[1]) + (p[2] + p[3]);
+        *(lds_u32x2*)(sp + qrow(rb) * PPITCH + 2 * (qkey(kb) + 4 * g)) = u32x2{lo, hi};
       }
-      mtrue[rb] = mt;
-      jumped |= mt > mref[rb] + kMaxJump;
+      mtrue[rb] = mt;   // raw score
+      jumped |= mt * a.scale_log2 > mref[rb] + kMaxJump;
       lround[rb] += sr;
       lexact[rb] += se;
     }
@@ -678,7 +686,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     if (*sm_redo == 0) break;
     // second pass: every row's reference is its true maximum over the item
 #pragma unroll
-    for (int rb = 0; rb < QRB; ++rb) mpreset[rb] = mtrue[rb];
+    for (int rb = 0; rb < QRB; ++rb) mpreset[rb] = mtrue[rb] * a.scale_log2;
     row_reduce_max(mpreset);
   }
   // accumulators of the last 8 PV MFMAs: 8 more wait states each, in write order
