@@ -343,34 +343,28 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   // Stage unit u into buffer u % NBUF.  Key rows past the tile's extent, and
   // rows of a page whose id is out of range, are zero-filled instead (never
   // read from the pool), so 0 * garbage never reaches the PV contraction.
+  // Returns the number of DMA instructions this wave issued (rows skipped
+  // above issue none), which the memory-counter waits below account for.
   auto issue_unit = [&](int u) {
     const uint32_t ub = (uint32_t)(u % NBUF) * (UK * 1024);
     const int kl = u * UK;                         // key offset within the split
     const int pid = __builtin_amdgcn_readfirstlane(sm_pid[pid0 + (kl >> 6)]);
     const bool pid_ok = (unsigned)pid < (unsigned)a.N;
     const uint16_t* pbase = a.pool + ((size_t)(pid_ok ? pid : 0) * PG + (kl & 63)) * D;
+    const int valid = pid_ok ? n_tile - (k_begin + kl) : 0;   // rows of the unit to fetch
 #pragma unroll 8
     for (int i = 0; i < ROWS_PW; ++i) {
       const int kap = w + 4 * i;                   // key row within the unit
-      if (pid_ok && k_begin + kl + kap < n_tile) {
+      if (kap < valid) {
         dma_row16(pbase + kap * D, dvoff[i & 3], lds0 + ub + (uint32_t)kap * 1024u);
       } else {
         *(lds_u32x4*)(sb + ub + kap * 1024 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
       }
     }
-  };
-  // DMA instructions this wave issued for unit u (rows skipped above issue none)
-  auto unit_ops = [&](int u) {
-    if (u >= n_units) return 0;
-    const int kl = u * UK;
-    const int pid = __builtin_amdgcn_readfirstlane(sm_pid[pid0 + (kl >> 6)]);
-    if ((unsigned)pid >= (unsigned)a.N) return 0;
-    const int valid = n_tile - (k_begin + kl);      // rows of the unit below n_tile
-    if (valid >= UK) return ROWS_PW;
-    int c = 0;
+    int ops = 0;
 #pragma unroll
-    for (int i = 0; i < ROWS_PW; ++i) c += (w + 4 * i) < valid;
-    return c;
+    for (int i = 0; i < ROWS_PW; ++i) ops += (w + 4 * i) < valid;
+    return ops;
   };
 
   // LDS byte offsets (within a unit buffer) of this lane's operand reads.
@@ -583,7 +577,10 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 
   // ---- the pipeline: NBUF - 1 units in flight ahead of the one computed.
   // A second pass runs only if some row's scores jumped past kMaxJump.
-  constexpr int AHEAD = NBUF - 1;
+  // Units in flight ahead of the one computed.  Row-split tiles (32-key
+  // units) keep two, not three: a deeper queue only moves the wait from the
+  // memory counter into the DMA issue, where the wave also stops computing.
+  constexpr int AHEAD = KS ? NBUF - 1 : 2;
 #pragma nounroll
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
@@ -604,9 +601,9 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     auto ring_get = [&](int v) { return (int)((ops_ring >> (8 * (v % NBUF))) & 0xFFu); };
     int issued = 0;       // units issued so far (uniform)
     auto issue_next = [&]() {
-      issue_unit(issued);
+      const int ops = issue_unit(issued);
       const uint32_t sh = 8u * (uint32_t)(issued % NBUF);
-      ops_ring = (ops_ring & ~(0xFFu << sh)) | ((uint32_t)unit_ops(issued) << sh);
+      ops_ring = (ops_ring & ~(0xFFu << sh)) | ((uint32_t)ops << sh);
       ++issued;
     };
     // Key-split tiles stage Q through the last buffer, first, so that Q can
