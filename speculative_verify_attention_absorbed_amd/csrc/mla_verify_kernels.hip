@@ -714,9 +714,12 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   __syncthreads();
 
   // ---- finalize: (-inf, 0) for rows without a visible key.  The scaled bf16
-  // rows are staged in the (now idle) key buffers, swizzled by 16-byte chunk,
-  // and then leave as whole 1 KiB rows, one store instruction per row.
-  static_assert(RT * 1024 <= kBufBytes, "row staging");
+  // rows are staged in the (now idle) key buffers and P tile at a pitch of
+  // 1040 bytes (16 consecutive rows start on 16 different bank groups, and a
+  // row's 16-dim blocks sit at fixed offsets), then leave as whole 1 KiB
+  // rows, one store instruction per row.
+  constexpr int SPITCH = 1040;
+  static_assert(RT * SPITCH <= kBufBytes + kPBytes, "row staging");
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     const int row = rb * 16 + i16;
@@ -727,17 +730,17 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       le += st_le[k * RT + row];
     }
     const bool empty = !(lr > 0.f);   // a visible key contributes P >= 1 (its max set the reference)
-    const float inv = empty ? 0.f : 1.f / lr;
+    const float inv = empty ? 0.f : __builtin_amdgcn_rcpf(lr);   // v_rcp_f32, 1 ulp
+    lds_u8* const rowp = sb + row * SPITCH + 256 * w + 8 * g;    // dims 128 w + 4 g of the row
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       const f32x4 v = o[dt][rb] * inv;
-      const u32x2 wv = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-      const int chunk = 16 * w + 2 * dt + (g >> 1);   // 16-byte chunk of dims 128 w + 16 dt + 4 g
-      *(lds_u32x2*)(sb + row * 1024 + 16 * (chunk ^ (row & 15)) + 8 * (g & 1)) = wv;
+      *(lds_u32x2*)(rowp + 32 * dt) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
     }
     if (w == 0 && g == 0 && row0 + row < a.R) {
       const size_t row_g = (size_t)b * a.R + row0 + row;
-      const float l = empty ? -INFINITY : (st_m[row] + log2f(le)) * kLn2;
+      // v_log_f32 is log2 with 1 ulp error
+      const float l = empty ? -INFINITY : (st_m[row] + __builtin_amdgcn_logf(le)) * kLn2;
       if (a.direct) a.lse[row_g] = l;
       else a.part_lse[(size_t)s * a.B * a.R + row_g] = l;
     }
@@ -761,7 +764,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < RPW; ++i) {
     const int row = w + 4 * i;
-    rowv[i] = *(const lds_u32x4*)(sb + row * 1024 + 16 * (lane ^ (row & 15)));
+    rowv[i] = *(const lds_u32x4*)(sb + row * SPITCH + 16 * lane);
   }
 #pragma unroll
   for (int i = 0; i < RPW; ++i)
