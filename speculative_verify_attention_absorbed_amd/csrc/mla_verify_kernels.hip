@@ -197,8 +197,9 @@ __device__ __forceinline__ void wait_vm_barrier(int allowed) {
 //       the splits of one request land on different dies, and split s of
 //       request b on die (b + s) mod 8 when S = 8: the first splits (never
 //       empty) rotate over the dies, and a ragged batch spreads evenly (used
-//       when a request has several row tiles: there the per-die load, not
-//       the Q re-read, decides the time).
+//       when a request has four or more row tiles, i.e. a large head fold:
+//       there the per-die load, not the re-read of Q on every die, decides
+//       the time).
 // The grid is 8 * ceil(groups / 8) * row_tiles workgroups; returns -1 for the
 // padding ones.
 static_assert((mla::kNumXCDs & (mla::kNumXCDs - 1)) == 0, "XCD count is a power of two");
@@ -263,7 +264,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
   const int g = lane >> 4, i16 = lane & 15;
 
-  int id = logical_item(blockIdx.x, a.B * a.S, a.row_tiles, a.row_tiles > 1);
+  int id = logical_item(blockIdx.x, a.B * a.S, a.row_tiles, a.row_tiles >= 4);
   if (id < 0) return;
   const int rt = id % a.row_tiles;
   id /= a.row_tiles;
@@ -277,16 +278,27 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   auto qrow = [&](int rb) { return (KS ? 0 : 32 * w) + 16 * rb + i16; };
   auto qkey = [&](int kb) { return KS ? 16 * w : 16 * kb; };
 
-  // ---- bounds of the tile's tokens (lane j: token t_lo + j; at most 16)
+  // ---- bounds of the tile's tokens (lane j: token t_lo + j; at most 16) and,
+  // when it fits, the request's whole block-table row (the split's page range
+  // is known only once the bounds are): both loads are issued before either
+  // value is used, so they share one memory round trip.
   const int t_lo = row0 / a.H;
   const int ntok = (row0 + rows_here - 1) / a.H - t_lo + 1;
-  const int tb = (lane < ntok) ? clampi(a.bounds[b * a.T + t_lo + lane], 0, max_keys) : 0;
-  // The request's whole block-table row, when it fits, is staged now, in the
-  // same memory round trip as the bounds (the split's page range is known
-  // only once the bounds are).
+  const int braw = a.bounds[b * a.T + min(t_lo + lane, a.T - 1)];
   const bool whole_row = a.P <= mla::kMaxSplitPages;
-  if (whole_row)
-    for (int i = tid; i < a.P; i += 256) sm_pid[i] = a.bt[b * a.P + i];
+  constexpr int kPidPerThread = mla::kMaxSplitPages / kThreads;
+  int pidv[kPidPerThread];
+  if (whole_row) {
+#pragma unroll
+    for (int j = 0; j < kPidPerThread; ++j)
+      pidv[j] = a.bt[(size_t)b * a.P + min(tid + kThreads * j, a.P - 1)];
+  }
+  const int tb = (lane < ntok) ? clampi(braw, 0, max_keys) : 0;
+  if (whole_row) {
+#pragma unroll
+    for (int j = 0; j < kPidPerThread; ++j)
+      if (tid + kThreads * j < a.P) sm_pid[tid + kThreads * j] = pidv[j];
+  }
 
   // ---- Q^T of this wave's QK rows, loaded in the pipeline prologue below:
   // row-split tiles load their own rows straight into registers, next to
