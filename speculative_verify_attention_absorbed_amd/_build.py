@@ -21,7 +21,10 @@ SOURCES = ["mla_verify_kernels.hip", "mla_verify_host.cpp"]
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops
 # (v_pk_fma_f32 and friends); it is a device-side feature flag.
-DEVICE_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# kernarg preload: the leading 10 kernel arguments arrive in SGPRs at wave
+# start instead of through a scalar memory round trip.
+DEVICE_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-kernarg-preload-count=10"]
 COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function"]
 
 

@@ -230,7 +230,24 @@ __device__ __forceinline__ int logical_item(int bid, int n_groups, int row_tiles
 // row's reference max is fixed there for the whole item; P may exceed 1
 // later (see kMaxJump for the second pass).
 template <int MODE>
-__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
+// The arguments the prologue needs first (the work-item decode, the bounds,
+// the block table and Q) lead the list as plain scalars, so that the command
+// processor preloads them into SGPRs (the library is built with a kernarg
+// preload count of 10); the rest stay in the argument block and are fetched
+// while the bounds are in flight.
+__global__ __launch_bounds__(256) void attn_kernel(const uint16_t* q, const int32_t* bt,
+                                                   const int32_t* bounds, int B, int S, int row_tiles,
+                                                   int T, int H, int R, int P, AttnArgs a) {
+  a.q = q;
+  a.bt = bt;
+  a.bounds = bounds;
+  a.B = B;
+  a.S = S;
+  a.row_tiles = row_tiles;
+  a.T = T;
+  a.H = H;
+  a.R = R;
+  a.P = P;
   constexpr bool KS = MODE < 2;                 // key-split QK
   constexpr int NRB = MODE == 0 ? 2 : (MODE == 1 ? 4 : 8);   // 16-row blocks of the tile
   constexpr int RT = 16 * NRB;                  // rows per tile
@@ -278,6 +295,27 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   auto qrow = [&](int rb) { return (KS ? 0 : 32 * w) + 16 * rb + i16; };
   auto qkey = [&](int kb) { return KS ? 16 * w : 16 * kb; };
 
+  // Lane offsets of the DMA of row w + 4i (a key row of a unit, or a Q row):
+  // its chunk order is swizzled by (w + 4i) & 15, which takes four values per
+  // wave.
+  uint32_t dvoff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) dvoff[j] = 16u * (uint32_t)(lane ^ swz16((w + 4 * j) & 15));
+
+  // ---- key-split tiles, where every wave needs every Q row, stage Q^T through
+  // the last unit buffer, issued first: its address needs only the tile, so it
+  // shares the memory round trip of the bounds below and is in LDS by the
+  // time the first unit is issued.
+  const uint32_t qb = (uint32_t)(NBUF - 1) * (UK * 1024);
+  if constexpr (KS) {
+#pragma unroll
+    for (int i = 0; i < RT / 4; ++i) {
+      const int r = w + 4 * i;
+      const uint16_t* src = a.q + ((size_t)b * a.R + min(row0 + r, a.R - 1)) * D;
+      dma_row16(src, dvoff[i & 3], lds0 + qb + (uint32_t)r * 1024u);
+    }
+  }
+
   // ---- bounds of the tile's tokens (lane j: token t_lo + j; at most 16) and,
   // when it fits, the request's whole block-table row (the split's page range
   // is known only once the bounds are): both loads are issued before either
@@ -287,12 +325,13 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   const int braw = a.bounds[b * a.T + min(t_lo + lane, a.T - 1)];
   const bool whole_row = a.P <= mla::kMaxSplitPages;
   constexpr int kPidPerThread = mla::kMaxSplitPages / kThreads;
-  int pidv[kPidPerThread];
-  if (whole_row) {
+  int pidv[kPidPerThread];   // loaded unconditionally (in-row addresses), used only for a whole row
 #pragma unroll
-    for (int j = 0; j < kPidPerThread; ++j)
-      pidv[j] = a.bt[(size_t)b * a.P + min(tid + kThreads * j, a.P - 1)];
-  }
+  for (int j = 0; j < kPidPerThread; ++j) pidv[j] = a.bt[(size_t)b * a.P + min(tid + kThreads * j, a.P - 1)];
+  // the rest of the arguments, fetched together while the bounds are in flight
+  asm volatile("" ::"s"(a.pool), "s"(a.out_lat), "s"(a.lse), "s"(a.part_o), "s"(a.part_lse), "s"(a.N),
+               "s"(a.scale_log2), "s"(a.direct), "s"(a.min_split_pages)
+               : "memory");
   const int tb = (lane < ntok) ? clampi(braw, 0, max_keys) : 0;
   if (whole_row) {
 #pragma unroll
@@ -300,10 +339,9 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       if (tid + kThreads * j < a.P) sm_pid[tid + kThreads * j] = pidv[j];
   }
 
-  // ---- Q^T of this wave's QK rows, loaded in the pipeline prologue below:
-  // row-split tiles load their own rows straight into registers, next to
-  // unit 0's pages; key-split tiles, where every wave needs every row, stage
-  // the tile once through LDS.
+  // ---- Q^T of this wave's QK rows: row-split tiles load their own rows
+  // straight into registers in the pipeline prologue below, next to unit 0's
+  // pages; key-split tiles move the staged tile from LDS there.
   bf16x8 qreg[QRB][16];   // qreg[rb][ks] = Q[tile row qrow(rb)][32 ks + 8 g .. +7]
 
   int n_tile = tb;
@@ -339,18 +377,13 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     // identity (lse = -inf), and the merge never reads their O
     for (int r = tid; r < rows_here; r += kThreads)
       a.part_lse[(size_t)s * a.B * a.R + (size_t)b * a.R + row0 + r] = -INFINITY;
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the Q staging has landed before LDS is released
     return;
   }
   if (!whole_row)
     for (int i = tid; i < p_end - p_begin; i += 256) sm_pid[i] = a.bt[b * a.P + p_begin + i];
   const int pid0 = whole_row ? p_begin : 0;   // sm_pid index of the split's first page
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-
-  // Lane offsets of the DMA of key row w + 4i: its chunk order is swizzled by
-  // (w + 4i) & 15, which takes four values per wave.
-  uint32_t dvoff[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) dvoff[j] = 16u * (uint32_t)(lane ^ swz16((w + 4 * j) & 15));
 
   // Stage unit u into buffer u % NBUF.  Key rows past the tile's extent, and
   // rows of a page whose id is out of range, are zero-filled instead (never
@@ -618,10 +651,9 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       ops_ring = (ops_ring & ~(0xFFu << sh)) | ((uint32_t)ops << sh);
       ++issued;
     };
-    // Key-split tiles stage Q through the last buffer, first, so that Q can
-    // reach the registers while unit 0 is still in flight.
+    // Key-split tiles move the staged Q to the registers while unit 0 is in
+    // flight.
     const bool stage_q = KS && pass == 0;
-    const uint32_t qb = (uint32_t)(NBUF - 1) * (UK * 1024);
     if constexpr (!KS) {
       if (pass == 0) {
 #pragma unroll
@@ -631,14 +663,6 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 #pragma unroll
           for (int ks = 0; ks < 16; ++ks) qreg[rb][ks] = __builtin_bit_cast(bf16x8, qp[ks * 4 + g]);
         }
-      }
-    }
-    if (stage_q) {
-#pragma unroll
-      for (int i = 0; i < RT / 4; ++i) {
-        const int r = w + 4 * i;
-        const uint16_t* src = a.q + ((size_t)b * a.R + min(row0 + r, a.R - 1)) * D;
-        dma_row16(src, dvoff[i & 3], lds0 + qb + (uint32_t)r * 1024u);
       }
     }
     if (n_units > 0) issue_next();
@@ -1100,11 +1124,14 @@ int run_attention(const mla_verify_params* p, const mla::Plan& pl, const mla_bf1
       (unsigned)((groups + mla::kNumXCDs - 1) / mla::kNumXCDs * mla::kNumXCDs * pl.row_tiles);
   const int mode = pl.shape.mode;
   if (mode == 0)
-    hipLaunchKernelGGL((attn_kernel<0>), dim3(grid), dim3(256), kAttnSmemBytes, stream, a);
+    hipLaunchKernelGGL((attn_kernel<0>), dim3(grid), dim3(256), kAttnSmemBytes, stream, a.q, a.bt, a.bounds,
+                       a.B, a.S, a.row_tiles, a.T, a.H, a.R, a.P, a);
   else if (mode == 1)
-    hipLaunchKernelGGL((attn_kernel<1>), dim3(grid), dim3(256), kAttnSmemBytes, stream, a);
+    hipLaunchKernelGGL((attn_kernel<1>), dim3(grid), dim3(256), kAttnSmemBytes, stream, a.q, a.bt, a.bounds,
+                       a.B, a.S, a.row_tiles, a.T, a.H, a.R, a.P, a);
   else if (mode == 2)
-    hipLaunchKernelGGL((attn_kernel<2>), dim3(grid), dim3(256), kAttnSmemBytes, stream, a);
+    hipLaunchKernelGGL((attn_kernel<2>), dim3(grid), dim3(256), kAttnSmemBytes, stream, a.q, a.bt, a.bounds,
+                       a.B, a.S, a.row_tiles, a.T, a.H, a.R, a.P, a);
   else
     return MLA_ERR_SHAPE;
   return launch_status();
