@@ -8,16 +8,20 @@
 // folded row has its own bound kv_bounds[b, r / H].
 //
 // Kernels:
-//   verify_attn_kernel   one workgroup per (request, 64-row tile, KV split).
-//                        4 waves x 16 rows.  Per 64-key page: the page is
-//                        staged HBM -> registers -> LDS (XOR-swizzled 16-byte
-//                        chunks); S^T = K Q^T on bf16 MFMA 16x16x32 with Q held
-//                        in registers; masked online softmax in fp32 (exp2
-//                        domain); O^T += V^T P^T on MFMA, where P^T stays in the
-//                        registers the S^T accumulators produced and V^T comes
-//                        from LDS through ds_read_tr16_b64 transposing reads.
-//                        Writes bf16 o_lat + lse directly (one split), or
-//                        normalised fp32 partials + partial lse (split-KV).
+//   attn_kernel<MODE>    one workgroup (4 waves) per (request, row tile, KV
+//                        split); tiles of 32, 64 or 128 folded rows.  The
+//                        split's pages stream HBM -> LDS by LDS-DMA
+//                        (XOR-swizzled 16-byte chunks) in 64- or 32-key units,
+//                        the next ones in flight while one is computed.
+//                        S^T = K Q^T on bf16 MFMA 16x16x32 with Q^T held in
+//                        registers; each row masked by its own bound; softmax
+//                        against a per-row reference max fixed on the split's
+//                        first unit (exp2 domain, fp32 sums); P in bf16 through
+//                        a small LDS tile; O^T += V^T P^T on MFMA with V^T read
+//                        by transposing LDS reads and O^T in accumulation
+//                        registers.  Writes bf16 o_lat + lse directly (one
+//                        split), or normalised bf16 partials + fp32 partial
+//                        lse (split-KV).
 //   combine_kernel       LSE merge of the S partials of every row (rows with
 //                        no visible key in any split give (-inf, 0)).
 //   gated_epilogue_kernel  per (head, 16 rows): LSE merge reading only the
