@@ -67,7 +67,7 @@ def round_bf16(a64: np.ndarray) -> np.ndarray:
 
 
 def assert_close_output(got: np.ndarray, want: np.ndarray, what: str, mask_rows=None):
-    """The benchmark spec bar: max-abs <= 1e-2 and relative L2 <= 5e-3."""
+    """Acceptance bar on outputs: max-abs <= 1e-2 and relative L2 <= 5e-3."""
     assert got.shape == want.shape, (got.shape, want.shape)
     assert np.all(np.isfinite(got)), f"{what}: non-finite values"
     diff = got - want
