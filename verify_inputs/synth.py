@@ -277,3 +277,49 @@ def referenced_kv_bytes(inp: VerifyInputs) -> int:
     """Bytes of KV a kernel must read: 1 KiB per visible key of each request."""
     n = np.clip(inp.kv_bounds.max(axis=1), 0, inp.block_table.shape[1] * PAGE)
     return int(n.sum()) * LATENT * 2
+
+
+@dataclasses.dataclass
+class KvUpdateInputs:
+    """One verify step's cache update.  bf16 arrays are uint16 bit patterns."""
+    pool: np.ndarray         # [N, 64, 512] bf16, dense
+    block_table: np.ndarray  # [B, P] int32, -1 past a request's pages
+    ctx: np.ndarray          # [B] int64 keys before the group
+    slots: np.ndarray        # [B, T] int32 write positions (-1 skip, some invalid)
+    new_latent: np.ndarray   # [B, T, 512] bf16
+    accepted: np.ndarray     # [B] int32 accepted drafts (some outside [0, T-1])
+
+
+def make_kv_update_inputs(*, batch, q_len, max_pages, pool_pages, seed, skip_frac=0.0,
+                          bad_frac=0.0, ctx=None, dense_pool=True) -> KvUpdateInputs:
+    """A seeded cache update: request b holds ``ctx[b]`` keys (uniform in
+    [0, max_pages*64 - q_len] unless given) and its group of ``q_len`` tokens
+    goes to positions ctx[b] .. ctx[b] + q_len - 1.  Each slot is replaced by
+    -1 with probability ``skip_frac`` (owned elsewhere) and by an invalid
+    value (>= max_pages*64 or below -1) with probability ``bad_frac``.  Pages
+    are distinct across requests, so valid slots never collide.  With
+    ``dense_pool=False`` no pool is drawn (``pool`` is None)."""
+    rng = np.random.default_rng(seed)
+    limit = max_pages * PAGE - q_len
+    if ctx is None:
+        ctx = rng.integers(0, limit + 1, size=batch)
+    ctx = np.asarray(ctx, dtype=np.int64).reshape(batch)
+    n_pages = (ctx + q_len + PAGE - 1) // PAGE
+    assert int(n_pages.sum()) <= pool_pages, "pool too small for distinct pages"
+    perm = rng.permutation(pool_pages)
+    table = np.full((batch, max_pages), -1, dtype=np.int32)
+    at = 0
+    for b in range(batch):
+        table[b, :n_pages[b]] = perm[at:at + n_pages[b]]
+        at += int(n_pages[b])
+    slots = (ctx[:, None] + np.arange(q_len)[None, :]).astype(np.int64)
+    u = rng.random((batch, q_len))
+    bad_vals = np.where(rng.random((batch, q_len)) < 0.5,
+                        rng.integers(max_pages * PAGE, max_pages * PAGE + 1000, size=(batch, q_len)),
+                        rng.integers(-1000, -1, size=(batch, q_len)))
+    slots = np.where(u < skip_frac, -1, np.where(u < skip_frac + bad_frac, bad_vals, slots))
+    new_latent = _normal_bf16(rng, (batch, q_len, LATENT), 1.0 / np.sqrt(LATENT))
+    accepted = rng.integers(-1, q_len + 1, size=batch).astype(np.int32)
+    # the pool is drawn last, so the other arrays do not depend on dense_pool
+    pool = _normal_bf16(rng, (pool_pages, PAGE, LATENT), 1.0 / np.sqrt(LATENT)) if dense_pool else None
+    return KvUpdateInputs(pool, table, ctx, slots.astype(np.int32), new_latent, accepted)
