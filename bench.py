@@ -182,6 +182,48 @@ def recorded_traffic(config):
 
 
 # --------------------------------------------------------------- main
+def kv_update_timings(args, x, pools, bt, timed, lib, torch, np):
+    """Per-call time of mla_verify_kv_append (the B*T group written by slot
+    table) and mla_verify_kv_trim, in the same launch mode as the call."""
+    dev = bt.device
+    b, t, _ = x.shape
+    pos = (np.asarray(x.ctx)[:, None] - t + np.arange(t)[None, :]).astype(np.int64)   # group positions
+    slots = torch.from_numpy(np.where(pos >= 0, pos, -1).astype(np.int32)).to(dev)
+    pos = np.maximum(pos, 0)
+    pages = torch.from_numpy(np.take_along_axis(x.block_table, pos // 64, axis=1).astype(np.int64)).to(dev)
+    rows = torch.from_numpy(pos % 64).to(dev)
+    group = pools[0][pages, rows].contiguous()          # [B, T, 512]: what those slots hold now
+    kv_len = torch.from_numpy(np.asarray(x.ctx, dtype=np.int32)).to(dev)
+    accepted = torch.from_numpy(np.random.default_rng(0).integers(0, t, size=b).astype(np.int32)).to(dev)
+    new_len = torch.empty_like(kv_len)
+    released = torch.empty_like(kv_len)
+    table = bt.clone()
+    vp = ctypes.c_void_p
+    n_sets = len(pools)
+    P, N = x.block_table.shape[1], x.pool.num_pages
+
+    def append(i, sh):
+        rc = lib.mla_verify_kv_append(b, t, P, N, vp(group.data_ptr()), vp(slots.data_ptr()),
+                                      vp(bt.data_ptr()), vp(pools[i % n_sets].data_ptr()), vp(0), sh)
+        if rc != 0:
+            raise RuntimeError(f"mla_verify_kv_append: {rc}")
+
+    def trim(i, sh):
+        rc = lib.mla_verify_kv_trim(b, t, P, vp(kv_len.data_ptr()), vp(accepted.data_ptr()),
+                                    vp(new_len.data_ptr()), vp(table.data_ptr()),
+                                    vp(released.data_ptr()), sh)
+        if rc != 0:
+            raise RuntimeError(f"mla_verify_kv_trim: {rc}")
+
+    steps = max(64, args.steps // 4)
+    a_ms, _, _ = timed(append, steps, 8)
+    t_ms, _, _ = timed(trim, steps, 8)
+    moved = b * t * 2 * 1024
+    return {"kv_append_us": round(a_ms * 1e3, 3), "kv_append_bytes": moved,
+            "kv_append_gbs": round(moved / (a_ms * 1e-3) / 1e9, 1),
+            "kv_trim_us": round(t_ms * 1e3, 3)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -348,6 +390,12 @@ def main():
         kms, _, _ = timed(attn_only, args.steps, args.warmup)
     ksec = kms * 1e-3
 
+    # ---- timed region 3 (reported in "extra", not in the value): the cache
+    # updates of the same step.  The append writes the group's own latents
+    # (gathered beforehand from the positions they already hold, so the pools
+    # do not change); the trim works on scratch copies of the lengths and table.
+    kv_us = kv_update_timings(args, x, pools, bt, timed, lib, torch, np)
+
     tokens = b * t
     bound = "mfma" if args.config == 5 else "hbm"
     k_gbs = alg["bytes"] / ksec / 1e9
@@ -388,7 +436,7 @@ def main():
                   "kernel_attention_tflops": round(k_tflops, 3),
                   "kernel_mfma_frac": round(k_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                   "kernel_kv_gbs": round(alg["kv_bytes"] / ksec / 1e9, 1),
-                  "kernel_source_sha": kernel_source_hash()},
+                  "kernel_source_sha": kernel_source_hash(), **kv_us},
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)

@@ -222,6 +222,57 @@ int mla_verify_absorb_q(const mla_verify_params* p,
                         mla_bf16* q_latent,
                         void* stream);
 
+/* KV append with a per-token slot table ("Kimi K3: DSpark speculative
+ * decoding under Helix CP", first commit message, "Per-token primitive" and
+ * "mla_rope_generation", and the same items under "Changes"): every token of
+ * a verify group carries its own rank-local KV write slot, -1 when the token
+ * is not owned here, and the per-token table supersedes a per-sequence gate.
+ * A slot is a request-logical key position (the key the attention calls
+ * address as j), so for every (b, t) with 0 <= slots[b,t] < P*64:
+ *     latent_kv_pages[block_table[b, slot / 64], slot % 64, :] = new_latent[b, t, :]
+ * The latent is written as given (NoPE: no rotary part).  Run it before the
+ * attention calls of the same step, whose bounds then cover the new keys.
+ *   new_latent       [B, T, 512] bf16   the group's compressed KV
+ *   slots            [B, T]      int32  write position, -1 = skip
+ *   block_table      [B, P]      int32
+ *   latent_kv_pages  [N, 64, 512] bf16  updated in place
+ *   bad_slots        int32 counter or NULL: incremented (device atomic) once
+ *                    for every token whose slot is below -1 or at least P*64,
+ *                    or whose page id lies outside [0, N); such a token writes
+ *                    nothing.  The caller zeroes it.
+ * Two tokens with the same slot: one of the two rows is written (which one
+ * is unspecified).  Shapes: 1 <= B, 1 <= T <= 16, P >= 1, N >= 1 (else
+ * MLA_ERR_SHAPE / MLA_ERR_ARG); pointers as for the other calls, bad_slots
+ * excepted (4-byte aligned or NULL). */
+int mla_verify_kv_append(int batch, int q_len, int max_pages_per_req, int num_pool_pages,
+                         const mla_bf16* new_latent,
+                         const int32_t* slots,
+                         const int32_t* block_table,
+                         mla_bf16* latent_kv_pages,
+                         int32_t* bad_slots,
+                         void* stream);
+
+/* Trim of rejected tails (first page, "What does this PR do?", "Speculative
+ * decoding": verification keeps the target token and the accepted drafts, and
+ * the KV cache trims the rejected tail).  Request b held kv_len[b] keys after
+ * the append, the group's T = k+1 tokens last; it keeps its target token and
+ * a = clamp(accepted[b], 0, T-1) drafts, so with L = clamp(kv_len[b], 0, P*64):
+ *     new_len[b] = max(0, L - (T - 1 - a))
+ * A page that held only dropped keys (page p with new_len <= 64 p < L; since
+ * T <= 16 there is at most one) is released: its id is written to
+ * released_page[b] and block_table[b, p] is set to -1; released_page[b] = -1
+ * when no page is released.
+ *   kv_len, accepted  [B] int32;  new_len [B] int32 (may alias kv_len);
+ *   block_table [B, P] int32 (updated in place);  released_page [B] int32.
+ * Shapes as mla_verify_kv_append. */
+int mla_verify_kv_trim(int batch, int q_len, int max_pages_per_req,
+                       const int32_t* kv_len,
+                       const int32_t* accepted,
+                       int32_t* new_len,
+                       int32_t* block_table,
+                       int32_t* released_page,
+                       void* stream);
+
 /* Static, human-readable text for a status code. */
 const char* mla_verify_status_string(int status);
 

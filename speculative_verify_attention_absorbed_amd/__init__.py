@@ -10,6 +10,8 @@ Entry points (same names as the C ABI, without the ``mla_`` prefix):
     verify_attn(...)        -> (out_latent [B,T,H,512] bf16, lse [B,T,H] f32)
     verify_attn_gated(...)  -> (out [B,T,H,128] bf16, lse, out_latent or None)
     verify_absorb_q(...)    -> q_latent [B,T,H,512] bf16
+    verify_kv_append(...)   -> None (writes the group's latents into the pool by slot table)
+    verify_kv_trim(...)     -> (new_len [B] i32, released_page [B] i32); block_table updated
     verify_attn_partials(...) -> (part_o [S,B*T*H,512] bf16, part_lse [S,B*T*H] f32)
     verify_lse_combine(...) -> (out_latent [rows,512] bf16, lse [rows] f32)
     verify_check / verify_num_splits / verify_tile_rows / verify_workspace_size / status_string
@@ -24,7 +26,8 @@ __all__ = [
     "MlaVerifyError", "VerifyParams", "lib_path", "load_library", "verify_check",
     "verify_num_splits", "verify_tile_rows", "verify_workspace_size", "verify_attn",
     "verify_attn_gated",
-    "verify_absorb_q", "verify_attn_partials", "verify_lse_combine", "status_string",
+    "verify_absorb_q", "verify_attn_partials", "verify_lse_combine", "verify_kv_append",
+    "verify_kv_trim", "status_string",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -40,7 +43,7 @@ LATENT, PAGE, NOPE = 512, 64, 128
 EXPORTED_SYMBOLS = [
     "mla_verify_check", "mla_verify_num_splits", "mla_verify_tile_rows", "mla_verify_workspace_size",
     "mla_verify_attn", "mla_verify_attn_partials", "mla_verify_lse_combine",
-    "mla_verify_attn_gated", "mla_verify_absorb_q",
+    "mla_verify_attn_gated", "mla_verify_absorb_q", "mla_verify_kv_append", "mla_verify_kv_trim",
     "mla_verify_status_string",
 ]
 
@@ -106,6 +109,11 @@ def load_library():
     lib.mla_verify_lse_combine.restype = ctypes.c_int
     lib.mla_verify_absorb_q.argtypes = [P, vp, vp, vp, vp]
     lib.mla_verify_absorb_q.restype = ctypes.c_int
+    i = ctypes.c_int
+    lib.mla_verify_kv_append.argtypes = [i, i, i, i, vp, vp, vp, vp, vp, vp]
+    lib.mla_verify_kv_append.restype = ctypes.c_int
+    lib.mla_verify_kv_trim.argtypes = [i, i, i, vp, vp, vp, vp, vp, vp]
+    lib.mla_verify_kv_trim.restype = ctypes.c_int
     lib.mla_verify_status_string.argtypes = [ctypes.c_int]
     lib.mla_verify_status_string.restype = ctypes.c_char_p
     _LIB = lib
@@ -341,3 +349,51 @@ def verify_absorb_q(q_nope, w_uk, *, q_latent=None, stream=None):
                                             _ptr(q_latent), _stream(stream))
     _check(rc, "mla_verify_absorb_q")
     return q_latent
+
+
+def verify_kv_append(new_latent, slots, block_table, latent_kv_pages, *, bad_slots=None, stream=None):
+    """``mla_verify_kv_append``: for every (b, t) with 0 <= slots[b, t] < P*64,
+    latent_kv_pages[block_table[b, slot // 64], slot % 64] = new_latent[b, t]
+    (in place).  ``bad_slots`` (int32 [1], optional) counts out-of-range
+    entries; -1 entries are skipped silently."""
+    torch = _torch()
+    bf = _bf16_types()
+    if new_latent.dim() != 3 or block_table.dim() != 2 or latent_kv_pages.dim() != 3:
+        raise ValueError("new_latent must be [B, T, 512], block_table [B, P], pool [N, 64, 512]")
+    b, t, _ = new_latent.shape
+    p = block_table.shape[1]
+    n = latent_kv_pages.shape[0]
+    _dev_tensor(new_latent, "new_latent", (b, t, LATENT), bf)
+    _dev_tensor(slots, "slots", (b, t), (torch.int32,))
+    _dev_tensor(block_table, "block_table", (b, p), (torch.int32,))
+    _dev_tensor(latent_kv_pages, "latent_kv_pages", (n, PAGE, LATENT), bf)
+    if bad_slots is not None:
+        _dev_tensor(bad_slots, "bad_slots", (1,), (torch.int32,))
+    rc = load_library().mla_verify_kv_append(int(b), int(t), int(p), int(n), _ptr(new_latent), _ptr(slots),
+                                             _ptr(block_table), _ptr(latent_kv_pages), _ptr(bad_slots),
+                                             _stream(stream))
+    _check(rc, "mla_verify_kv_append")
+
+
+def verify_kv_trim(kv_len, accepted, block_table, q_len, *, new_len=None, released_page=None, stream=None):
+    """``mla_verify_kv_trim``: drops the rejected tail of every request's group
+    (block_table is updated in place).  Returns (new_len, released_page)."""
+    torch = _torch()
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [B, P]")
+    b, p = block_table.shape
+    i32 = (torch.int32,)
+    _dev_tensor(kv_len, "kv_len", (b,), i32)
+    _dev_tensor(accepted, "accepted", (b,), i32)
+    _dev_tensor(block_table, "block_table", (b, p), i32)
+    if new_len is None:
+        new_len = torch.empty((b,), dtype=torch.int32, device=kv_len.device)
+    if released_page is None:
+        released_page = torch.empty((b,), dtype=torch.int32, device=kv_len.device)
+    _dev_tensor(new_len, "new_len", (b,), i32)
+    _dev_tensor(released_page, "released_page", (b,), i32)
+    rc = load_library().mla_verify_kv_trim(int(b), int(q_len), int(p), _ptr(kv_len), _ptr(accepted),
+                                           _ptr(new_len), _ptr(block_table), _ptr(released_page),
+                                           _stream(stream))
+    _check(rc, "mla_verify_kv_trim")
+    return new_len, released_page

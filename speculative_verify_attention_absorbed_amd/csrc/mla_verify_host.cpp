@@ -93,6 +93,16 @@ Plan make_plan(const mla_verify_params* p, bool gated) {
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
+int check_kv_dims(int batch, int q_len, int max_pages_per_req, int num_pool_pages) {
+  if (batch < 1 || q_len < 1 || q_len > MLA_VERIFY_MAX_Q_LEN) return MLA_ERR_SHAPE;
+  if (max_pages_per_req < 1 || num_pool_pages < 1) return MLA_ERR_ARG;
+  // slot and table indices stay inside int32
+  if ((int64_t)max_pages_per_req * MLA_VERIFY_PAGE > (int64_t)1 << 30) return MLA_ERR_ARG;
+  if ((int64_t)batch * max_pages_per_req > (int64_t)1 << 30) return MLA_ERR_ARG;
+  if ((int64_t)batch * q_len > (int64_t)1 << 24) return MLA_ERR_SHAPE;
+  return MLA_OK;
+}
+
 }  // namespace mla
 
 extern "C" {

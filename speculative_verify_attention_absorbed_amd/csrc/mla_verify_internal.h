@@ -37,6 +37,8 @@ TileShape choose_shape(int rows, int batch);
 int check_params(const mla_verify_params* p);
 Plan make_plan(const mla_verify_params* p, bool gated);
 bool aligned16(const void* ptr);
+// Sizes of the KV append / trim calls (pure host checks).
+int check_kv_dims(int batch, int q_len, int max_pages_per_req, int num_pool_pages);
 
 }  // namespace mla
 

@@ -136,6 +136,34 @@ def test_entry_points_validate_before_any_hip_call(lib):
     assert lib.mla_verify_attn(None, *args, z, 0, z) == -1
 
 
+def test_kv_update_entry_points_validate_before_any_hip_call(lib):
+    """KV append / trim: bad sizes and pointers come back as error codes."""
+    i = ctypes.c_int
+    lib.mla_verify_kv_append.argtypes = [i, i, i, i] + [ctypes.c_void_p] * 6
+    lib.mla_verify_kv_trim.argtypes = [i, i, i] + [ctypes.c_void_p] * 6
+    fake = ctypes.c_void_p(0x1000)
+    odd = ctypes.c_void_p(0x1002)
+    z = ctypes.c_void_p(0)
+    ok4 = [fake] * 4
+    # sizes
+    assert lib.mla_verify_kv_append(0, 8, 4, 16, *ok4, z, z) == -2
+    assert lib.mla_verify_kv_append(2, 0, 4, 16, *ok4, z, z) == -2
+    assert lib.mla_verify_kv_append(2, 17, 4, 16, *ok4, z, z) == -2
+    assert lib.mla_verify_kv_append(2, 8, 0, 16, *ok4, z, z) == -4
+    assert lib.mla_verify_kv_append(2, 8, 4, 0, *ok4, z, z) == -4
+    assert lib.mla_verify_kv_append(2, 8, 1 << 25, 16, *ok4, z, z) == -4
+    # pointers: NULL, misaligned, and a misaligned counter
+    assert lib.mla_verify_kv_append(2, 8, 4, 16, z, fake, fake, fake, z, z) == -1
+    assert lib.mla_verify_kv_append(2, 8, 4, 16, fake, fake, fake, z, z, z) == -1
+    assert lib.mla_verify_kv_append(2, 8, 4, 16, fake, odd, fake, fake, z, z) == -4
+    assert lib.mla_verify_kv_append(2, 8, 4, 16, *ok4, ctypes.c_void_p(0x1001), z) == -4
+    assert lib.mla_verify_kv_trim(0, 8, 4, *[fake] * 5, z) == -2
+    assert lib.mla_verify_kv_trim(2, 17, 4, *[fake] * 5, z) == -2
+    assert lib.mla_verify_kv_trim(2, 8, 0, *[fake] * 5, z) == -4
+    assert lib.mla_verify_kv_trim(2, 8, 4, fake, fake, z, fake, fake, z) == -1
+    assert lib.mla_verify_kv_trim(2, 8, 4, fake, fake, fake, odd, fake, z) == -4
+
+
 def test_tile_rows_forced_and_resolved(lib):
     # forced tiles are honoured for any head fold; 0 resolves to one of 32/64/128
     for t in (32, 64, 128):
