@@ -17,7 +17,7 @@ LIB_NAME = "libmla_verify.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["mla_verify_kernels.hip", "mla_verify_host.cpp"]
+SOURCES = ["mla_verify_kernels.hip", "mla_kv_update.hip", "mla_verify_host.cpp"]
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops
 # (v_pk_fma_f32 and friends); it is a device-side feature flag.

@@ -3,6 +3,7 @@
 // exercised on a machine without a GPU.
 #include <cmath>
 #include <cstdint>
+#include <initializer_list>
 
 #include "mla_verify.h"
 #include "mla_verify_internal.h"
@@ -92,6 +93,18 @@ Plan make_plan(const mla_verify_params* p, bool gated) {
 }
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+bool any_null(std::initializer_list<const void*> ptrs) {
+  for (const void* x : ptrs)
+    if (x == nullptr) return true;
+  return false;
+}
+
+bool any_misaligned(std::initializer_list<const void*> ptrs) {
+  for (const void* x : ptrs)
+    if (x != nullptr && !aligned16(x)) return true;
+  return false;
+}
 
 int check_kv_dims(int batch, int q_len, int max_pages_per_req, int num_pool_pages) {
   if (batch < 1 || q_len < 1 || q_len > MLA_VERIFY_MAX_Q_LEN) return MLA_ERR_SHAPE;

@@ -4,6 +4,7 @@
 #define MLA_VERIFY_INTERNAL_H
 
 #include <cstddef>
+#include <initializer_list>
 
 #include "mla_verify.h"
 
@@ -37,6 +38,12 @@ TileShape choose_shape(int rows, int batch);
 int check_params(const mla_verify_params* p);
 Plan make_plan(const mla_verify_params* p, bool gated);
 bool aligned16(const void* ptr);
+bool any_null(std::initializer_list<const void*> ptrs);
+bool any_misaligned(std::initializer_list<const void*> ptrs);   // any non-null pointer not 16-byte aligned
+// Device set-up check (gfx950, kernel attributes) and the status of the last
+// launch on this thread; defined with the attention kernels.
+int device_ready();
+int launch_result();
 // Sizes of the KV append / trim calls (pure host checks).
 int check_kv_dims(int batch, int q_len, int max_pages_per_req, int num_pool_pages);
 

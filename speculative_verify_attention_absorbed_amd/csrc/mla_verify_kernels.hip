@@ -28,10 +28,7 @@
 //                        partials with a nonzero weight, then W_UV (512 -> 128)
 //                        on MFMA and the sigmoid gate; optional o_lat output.
 //   absorb_q_kernel      q_latent = W_UK[h]^T q_nope, fp32 accumulate, bf16.
-//   kv_append_kernel     the group's latents into the paged cache by a
-//                        per-token slot table (-1 = skip).
-//   kv_trim_kernel       rejected tails dropped: new lengths, and the page
-//                        that held only dropped keys released.
+// The paged-cache updates (KV append, trim) live in mla_kv_update.hip.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -1040,54 +1037,6 @@ __global__ __launch_bounds__(kThreads, 3) void gated_epilogue_kernel(
   }
 }
 
-// KV append with a per-token slot table: one wave per token of a group; its
-// 1 KiB latent row goes to the page and slot its table entry names (-1:
-// another rank owns the token, nothing to write).  Out-of-range slots and
-// page ids write nothing and are counted.
-__global__ __launch_bounds__(kThreads) void kv_append_kernel(const uint16_t* __restrict__ new_latent,
-                                                             const int32_t* __restrict__ slots,
-                                                             const int32_t* __restrict__ bt,
-                                                             uint16_t* __restrict__ pool,
-                                                             int32_t* __restrict__ bad, int tokens, int T,
-                                                             int P, int N) {
-  const int tok = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (tok >= tokens) return;
-  const int lane = threadIdx.x & 63;
-  const int b = tok / T;
-  const int slot = __builtin_amdgcn_readfirstlane(slots[tok]);
-  if (slot == -1) return;
-  const bool in_row = slot >= 0 && slot < P * PG;
-  const int pid = in_row ? __builtin_amdgcn_readfirstlane(bt[(size_t)b * P + slot / PG]) : -1;
-  if (!in_row || pid < 0 || pid >= N) {
-    if (lane == 0 && bad != nullptr) atomicAdd(bad, 1);
-    return;
-  }
-  const uint4 v = *reinterpret_cast<const uint4*>(new_latent + (size_t)tok * D + lane * 8);
-  *reinterpret_cast<uint4*>(pool + ((size_t)pid * PG + (slot & (PG - 1))) * D + lane * 8) = v;
-}
-
-// Trim of rejected tails: one thread per request.  The dropped keys are the
-// last T - 1 - accepted (< 16 < 64) of the request, so at most one page holds
-// nothing but dropped keys; it is released from the block table.
-__global__ __launch_bounds__(kThreads) void kv_trim_kernel(const int32_t* kv_len, const int32_t* accepted,
-                                                           int32_t* new_len, int32_t* bt, int32_t* released,
-                                                           int B, int T, int P) {
-  const int b = blockIdx.x * kThreads + threadIdx.x;
-  if (b >= B) return;
-  const int L = clampi(kv_len[b], 0, P * PG);
-  const int a = clampi(accepted[b], 0, T - 1);
-  const int nl = max(0, L - (T - 1 - a));
-  const int p_lo = (nl + PG - 1) / PG, p_hi = (L + PG - 1) / PG;
-  int rel = -1;
-  if (p_lo < p_hi) {
-    int32_t* e = bt + (size_t)b * P + p_lo;
-    rel = *e;
-    *e = -1;
-  }
-  new_len[b] = nl;
-  released[b] = rel;
-}
-
 // q_latent[row][c] = sum_d q_nope[row][d] * W_UK[h][d][c]; one workgroup per
 // (head, 16 rows); thread owns columns tid and tid + 256.
 __global__ __launch_bounds__(kThreads) void absorb_q_kernel(const uint16_t* __restrict__ q_nope,
@@ -1207,18 +1156,12 @@ int run_attention(const mla_verify_params* p, const mla::Plan& pl, const mla_bf1
   return launch_status();
 }
 
-bool any_null(std::initializer_list<const void*> ptrs) {
-  for (const void* x : ptrs)
-    if (x == nullptr) return true;
-  return false;
-}
-bool any_misaligned(std::initializer_list<const void*> ptrs) {
-  for (const void* x : ptrs)
-    if (x != nullptr && !mla::aligned16(x)) return true;
-  return false;
-}
-
 }  // namespace
+
+namespace mla {
+int device_ready() { return ensure_device(); }
+int launch_result() { return launch_status(); }
+}  // namespace mla
 
 extern "C" {
 
@@ -1228,8 +1171,8 @@ int mla_verify_attn(const mla_verify_params* p, const mla_bf16* q_latent,
                     size_t workspace_bytes, void* stream) {
   int rc = mla::check_params(p);
   if (rc != MLA_OK) return rc;
-  if (any_null({q_latent, latent_kv_pages, block_table, kv_bounds, out_latent, lse})) return MLA_ERR_NULL;
-  if (any_misaligned({q_latent, latent_kv_pages, block_table, kv_bounds, out_latent, lse, workspace}))
+  if (mla::any_null({q_latent, latent_kv_pages, block_table, kv_bounds, out_latent, lse})) return MLA_ERR_NULL;
+  if (mla::any_misaligned({q_latent, latent_kv_pages, block_table, kv_bounds, out_latent, lse, workspace}))
     return MLA_ERR_ARG;
   const mla::Plan pl = mla::make_plan(p, false);
   if (pl.workspace_bytes > 0 && (workspace == nullptr || workspace_bytes < pl.workspace_bytes))
@@ -1254,8 +1197,8 @@ int mla_verify_attn_partials(const mla_verify_params* p, const mla_bf16* q_laten
                              void* stream) {
   int rc = mla::check_params(p);
   if (rc != MLA_OK) return rc;
-  if (any_null({q_latent, latent_kv_pages, block_table, kv_bounds, part_o, part_lse})) return MLA_ERR_NULL;
-  if (any_misaligned({q_latent, latent_kv_pages, block_table, kv_bounds, part_o, part_lse}))
+  if (mla::any_null({q_latent, latent_kv_pages, block_table, kv_bounds, part_o, part_lse})) return MLA_ERR_NULL;
+  if (mla::any_misaligned({q_latent, latent_kv_pages, block_table, kv_bounds, part_o, part_lse}))
     return MLA_ERR_ARG;
   const mla::Plan pl = mla::make_plan(p, false);
   rc = ensure_device();
@@ -1267,8 +1210,8 @@ int mla_verify_attn_partials(const mla_verify_params* p, const mla_bf16* q_laten
 int mla_verify_lse_combine(int num_splits, int rows, const mla_bf16* part_o, const float* part_lse,
                            mla_bf16* out_latent, float* lse, void* stream) {
   if (num_splits < 1 || num_splits > MLA_VERIFY_MAX_SPLITS || rows < 1) return MLA_ERR_ARG;
-  if (any_null({part_o, part_lse, out_latent, lse})) return MLA_ERR_NULL;
-  if (any_misaligned({part_o, part_lse, out_latent, lse})) return MLA_ERR_ARG;
+  if (mla::any_null({part_o, part_lse, out_latent, lse})) return MLA_ERR_NULL;
+  if (mla::any_misaligned({part_o, part_lse, out_latent, lse})) return MLA_ERR_ARG;
   const int rc = ensure_device();
   if (rc != MLA_OK) return rc;
   hipLaunchKernelGGL(combine_kernel, dim3((rows + 3) / 4), dim3(kThreads), 0,
@@ -1285,9 +1228,9 @@ int mla_verify_attn_gated(const mla_verify_params* p, const mla_bf16* q_latent,
                           void* stream) {
   int rc = mla::check_params(p);
   if (rc != MLA_OK) return rc;
-  if (any_null({q_latent, latent_kv_pages, block_table, kv_bounds, w_uv, gate_logits, out, lse}))
+  if (mla::any_null({q_latent, latent_kv_pages, block_table, kv_bounds, w_uv, gate_logits, out, lse}))
     return MLA_ERR_NULL;
-  if (any_misaligned({q_latent, latent_kv_pages, block_table, kv_bounds, w_uv, gate_logits, out, lse,
+  if (mla::any_misaligned({q_latent, latent_kv_pages, block_table, kv_bounds, w_uv, gate_logits, out, lse,
                       out_latent, workspace}))
     return MLA_ERR_ARG;
   const mla::Plan pl = mla::make_plan(p, true);
@@ -1320,46 +1263,14 @@ int mla_verify_absorb_q(const mla_verify_params* p, const mla_bf16* q_nope, cons
                         mla_bf16* q_latent, void* stream) {
   int rc = mla::check_params(p);
   if (rc != MLA_OK) return rc;
-  if (any_null({q_nope, w_uk, q_latent})) return MLA_ERR_NULL;
-  if (any_misaligned({q_nope, w_uk, q_latent})) return MLA_ERR_ARG;
+  if (mla::any_null({q_nope, w_uk, q_latent})) return MLA_ERR_NULL;
+  if (mla::any_misaligned({q_nope, w_uk, q_latent})) return MLA_ERR_ARG;
   rc = ensure_device();
   if (rc != MLA_OK) return rc;
   const int bt_rows = p->batch * p->q_len;
   const unsigned grid = (unsigned)(((bt_rows + 15) / 16) * p->num_heads);
   hipLaunchKernelGGL(absorb_q_kernel, dim3(grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
                      q_nope, w_uk, q_latent, bt_rows, p->num_heads);
-  return launch_status();
-}
-
-int mla_verify_kv_append(int batch, int q_len, int max_pages_per_req, int num_pool_pages,
-                         const mla_bf16* new_latent, const int32_t* slots, const int32_t* block_table,
-                         mla_bf16* latent_kv_pages, int32_t* bad_slots, void* stream) {
-  int rc = mla::check_kv_dims(batch, q_len, max_pages_per_req, num_pool_pages);
-  if (rc != MLA_OK) return rc;
-  if (any_null({new_latent, slots, block_table, latent_kv_pages})) return MLA_ERR_NULL;
-  if (any_misaligned({new_latent, slots, block_table, latent_kv_pages})) return MLA_ERR_ARG;
-  if ((reinterpret_cast<uintptr_t>(bad_slots) & 3u) != 0) return MLA_ERR_ARG;
-  rc = ensure_device();
-  if (rc != MLA_OK) return rc;
-  const int tokens = batch * q_len;
-  hipLaunchKernelGGL(kv_append_kernel, dim3((tokens + 3) / 4), dim3(kThreads), 0,
-                     static_cast<hipStream_t>(stream), new_latent, slots, block_table, latent_kv_pages,
-                     bad_slots, tokens, q_len, max_pages_per_req, num_pool_pages);
-  return launch_status();
-}
-
-int mla_verify_kv_trim(int batch, int q_len, int max_pages_per_req, const int32_t* kv_len,
-                       const int32_t* accepted, int32_t* new_len, int32_t* block_table,
-                       int32_t* released_page, void* stream) {
-  int rc = mla::check_kv_dims(batch, q_len, max_pages_per_req, 1);
-  if (rc != MLA_OK) return rc;
-  if (any_null({kv_len, accepted, new_len, block_table, released_page})) return MLA_ERR_NULL;
-  if (any_misaligned({kv_len, accepted, new_len, block_table, released_page})) return MLA_ERR_ARG;
-  rc = ensure_device();
-  if (rc != MLA_OK) return rc;
-  hipLaunchKernelGGL(kv_trim_kernel, dim3((batch + kThreads - 1) / kThreads), dim3(kThreads), 0,
-                     static_cast<hipStream_t>(stream), kv_len, accepted, new_len, block_table,
-                     released_page, batch, q_len, max_pages_per_req);
   return launch_status();
 }
 
