@@ -27,7 +27,8 @@
 //   gated_epilogue_kernel  per (head, 16 rows): LSE merge reading only the
 //                        partials with a nonzero weight, then W_UV (512 -> 128)
 //                        on MFMA and the sigmoid gate; optional o_lat output.
-//   absorb_q_kernel      q_latent = W_UK[h]^T q_nope, fp32 accumulate, bf16.
+//   absorb_q_kernel      q_latent = W_UK[h]^T q_nope on bf16 MFMA (fp32
+//                        accumulate, bf16 out), W_UK[h] staged in LDS.
 // The paged-cache updates (KV append, trim) live in mla_kv_update.hip.
 #include <hip/hip_runtime.h>
 
@@ -1037,41 +1038,109 @@ __global__ __launch_bounds__(kThreads, 3) void gated_epilogue_kernel(
   }
 }
 
-// q_latent[row][c] = sum_d q_nope[row][d] * W_UK[h][d][c]; one workgroup per
-// (head, 16 rows); thread owns columns tid and tid + 256.
+// q_latent[row][c] = sum_d q_nope[row][d] * W_UK[h][d][c] on bf16 MFMA.
+// One workgroup per (head h, 64-row tile): W_UK[h] (128 x 512, 128 KiB) is
+// staged into LDS by DMA in the key-row layout of the attention kernel (a
+// 1 KiB row per d, 16-byte chunks XOR-swizzled), so its transposed MFMA
+// operand comes from the same conflict-free transposing reads as V^T there:
+//   Q_lat^T[c][row] = sum_d W^T[c][d] Q_nope^T[d][row]
+// with A = W^T blocks (16 c x 32 d) from LDS and B = q_nope blocks (32 d x
+// 16 rows) straight from memory.  Wave w owns columns 128 w .. +127 of all
+// 64 rows (8 x 4 blocks, 4 k-steps: 128 MFMAs).  Work items are laid out so
+// that the row tiles of one head run on one XCD and share W_UK[h] in its L2.
+constexpr int kAbsorbRows = 64;
+constexpr int kAbsorbSmemBytes = DV * D * 2;   // W_UK[h]: 128 rows of 1 KiB
 __global__ __launch_bounds__(kThreads) void absorb_q_kernel(const uint16_t* __restrict__ q_nope,
                                                             const uint16_t* __restrict__ w_uk,
                                                             uint16_t* __restrict__ q_lat, int BT, int H) {
-  __shared__ float qs[16][DV];
-  const int h = blockIdx.x % H;
-  const int rr0 = (blockIdx.x / H) * 16;
-  const int tid = threadIdx.x;
-  for (int e = tid; e < 16 * DV; e += kThreads) {
-    const int r = e / DV, d = e % DV;
-    const int rr = rr0 + r;
-    qs[r][d] = rr < BT ? bf16_to_f32(q_nope[((size_t)rr * H + h) * DV + d]) : 0.f;
-  }
-  __syncthreads();
-  float acc0[16], acc1[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) acc0[r] = acc1[r] = 0.f;
+  extern __shared__ uint4 smem[];
+  lds_u8* const sb = (lds_u8*)smem;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)sb;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, i16 = lane & 15;
+  const int tiles = (BT + kAbsorbRows - 1) / kAbsorbRows;
+  const int items = H * tiles;
+  const int per = (items + mla::kNumXCDs - 1) / mla::kNumXCDs;   // items per XCD slot run
+  const int item = (blockIdx.x % mla::kNumXCDs) * per + blockIdx.x / mla::kNumXCDs;
+  if (item >= items) return;
+  const int h = item / tiles;
+  const int row0 = (item % tiles) * kAbsorbRows;
+
+  // ---- W_UK[h] -> LDS: row d = w + 4 i, chunk order swizzled by d & 15
   const uint16_t* wh = w_uk + (size_t)h * DV * D;
-  for (int d = 0; d < DV; ++d) {
-    const float w0 = bf16_to_f32(wh[d * D + tid]);
-    const float w1 = bf16_to_f32(wh[d * D + tid + 256]);
+  uint32_t dvoff[4];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      acc0[r] = fmaf(qs[r][d], w0, acc0[r]);
-      acc1[r] = fmaf(qs[r][d], w1, acc1[r]);
+  for (int j = 0; j < 4; ++j) dvoff[j] = 16u * (uint32_t)(lane ^ swz16((w + 4 * j) & 15));
+#pragma unroll 8
+  for (int i = 0; i < DV / 4; ++i) {
+    const int d = w + 4 * i;
+    dma_row16(wh + (size_t)d * D, dvoff[i & 3], lds0 + (uint32_t)d * 1024u);
+  }
+  // ---- q_nope^T operands of the tile, from memory meanwhile:
+  // qop[rb][kk] = q_nope[row 16 rb + i16][32 kk + 8 g .. +7] (zero past BT)
+  bf16x8 qop[4][4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    const int row = row0 + 16 * rb + i16;
+    const uint4* src = reinterpret_cast<const uint4*>(q_nope + ((size_t)min(row, BT - 1) * H + h) * DV);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const uint4 v = row < BT ? src[4 * kk + g] : make_uint4(0, 0, 0, 0);
+      qop[rb][kk] = __builtin_bit_cast(bf16x8, v);
     }
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMAs and loads
+  __syncthreads();                       // every wave's rows of W are in LDS
+
+  // transposing-read offsets (as for V^T in the attention kernel, d = "key")
+  uint32_t trow[2];
+  int tsw[2];
+  {
+    const int q = i16 >> 2, e4 = i16 & 3;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int rr = rr0 + r;
-    if (rr >= BT) break;
-    uint16_t* dst = q_lat + ((size_t)rr * H + h) * D;
-    dst[tid] = bf16_bits(acc0[r]);
-    dst[tid + 256] = bf16_bits(acc1[r]);
+    for (int hi = 0; hi < 2; ++hi) {
+      const int k32 = 8 * g + q + 4 * hi;
+      const int sv = swz16(k32 & 15);
+      tsw[hi] = sv >> 1;
+      trow[hi] = (uint32_t)(k32 * 1024 + 16 * ((e4 >> 1) ^ (sv & 1)) + 8 * (e4 & 1));
+    }
+  }
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) acc[dt][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    const int c16 = 8 * w + dt;   // 16-column block of the output
+    bf16x8 wop[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const uint32_t base = 32768u * kk + 256u * (uint32_t)(c16 >> 3);
+      const uint32_t o0 = base + trow[0] + 32u * (uint32_t)((c16 & 7) ^ tsw[0]);
+      const uint32_t o1 = base + trow[1] + 32u * (uint32_t)((c16 & 7) ^ tsw[1]);
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sb + o0));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sb + o1));
+      wop[kk] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        acc[dt][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wop[kk], qop[rb][kk], acc[dt][rb], 0, 0, 0);
+  }
+  // ---- acc[dt][rb][i] = q_lat[row 16 rb + i16][col 128 w + 16 dt + 4 g + i]
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    const int row = row0 + 16 * rb + i16;
+    if (row >= BT) continue;
+    uint16_t* dst = q_lat + ((size_t)row * H + h) * D + 128 * w + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const f32x4 v = acc[dt][rb];
+      *reinterpret_cast<u32x2*>(dst + 16 * dt) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    }
   }
 }
 
@@ -1096,6 +1165,8 @@ int ensure_device() {
       for (const void* f : attn)
         fail |= hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kAttnSmemBytes) !=
                 hipSuccess;
+      fail |= hipFuncSetAttribute(reinterpret_cast<const void*>(absorb_q_kernel),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, kAbsorbSmemBytes) != hipSuccess;
       if (fail)
         return MLA_ERR_HIP;
     }
@@ -1268,9 +1339,10 @@ int mla_verify_absorb_q(const mla_verify_params* p, const mla_bf16* q_nope, cons
   rc = ensure_device();
   if (rc != MLA_OK) return rc;
   const int bt_rows = p->batch * p->q_len;
-  const unsigned grid = (unsigned)(((bt_rows + 15) / 16) * p->num_heads);
-  hipLaunchKernelGGL(absorb_q_kernel, dim3(grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
-                     q_nope, w_uk, q_latent, bt_rows, p->num_heads);
+  const int items = ((bt_rows + kAbsorbRows - 1) / kAbsorbRows) * p->num_heads;
+  const unsigned grid = (unsigned)((items + mla::kNumXCDs - 1) / mla::kNumXCDs * mla::kNumXCDs);
+  hipLaunchKernelGGL(absorb_q_kernel, dim3(grid), dim3(kThreads), kAbsorbSmemBytes,
+                     static_cast<hipStream_t>(stream), q_nope, w_uk, q_latent, bt_rows, p->num_heads);
   return launch_status();
 }
 
