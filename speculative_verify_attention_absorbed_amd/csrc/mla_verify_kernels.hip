@@ -1039,20 +1039,30 @@ __global__ __launch_bounds__(kThreads, 3) void gated_epilogue_kernel(
 }
 
 // q_latent[row][c] = sum_d q_nope[row][d] * W_UK[h][d][c] on bf16 MFMA.
-// One workgroup per (head h, 64-row tile): W_UK[h] (128 x 512, 128 KiB) is
-// staged into LDS by DMA in the key-row layout of the attention kernel (a
-// 1 KiB row per d, 16-byte chunks XOR-swizzled), so its transposed MFMA
-// operand comes from the same conflict-free transposing reads as V^T there:
+// One workgroup per (head h, 64-row tile, block of COLS output columns):
+// the 128 x COLS block of W_UK[h] is staged into LDS by DMA as one row of
+// 2 COLS bytes per d, whose 16-byte chunks are XOR-swizzled by d & 15 within
+// every 256-byte group exactly as an attention key row is, so its transposed
+// MFMA operand comes from the same conflict-free transposing reads as V^T
+// there:
 //   Q_lat^T[c][row] = sum_d W^T[c][d] Q_nope^T[d][row]
 // with A = W^T blocks (16 c x 32 d) from LDS and B = q_nope blocks (32 d x
-// 16 rows) straight from memory.  Wave w owns columns 128 w .. +127 of all
-// 64 rows (8 x 4 blocks, 4 k-steps: 128 MFMAs).  Work items are laid out so
-// that the row tiles of one head run on one XCD and share W_UK[h] in its L2.
+// 16 rows) straight from memory.  Wave w owns columns COLS/4 * w .. of the
+// block for all 64 rows (4 k-steps).  COLS = 512 (128 KiB of LDS, 128
+// MFMAs per wave) when there are enough (head, tile) items to fill the GPU;
+// COLS = 128 (32 KiB, 32 MFMAs) spreads a small batch over four times as many
+// workgroups.  Work items are laid out so that the workgroups of one head run
+// on one XCD and share W_UK[h] in its L2.
 constexpr int kAbsorbRows = 64;
-constexpr int kAbsorbSmemBytes = DV * D * 2;   // W_UK[h]: 128 rows of 1 KiB
+template <int COLS>
 __global__ __launch_bounds__(kThreads) void absorb_q_kernel(const uint16_t* __restrict__ q_nope,
                                                             const uint16_t* __restrict__ w_uk,
                                                             uint16_t* __restrict__ q_lat, int BT, int H) {
+  static_assert(COLS == 128 || COLS == 512, "column block");
+  constexpr int RB = COLS * 2;                 // bytes per staged row
+  constexpr int RPD = 1024 / RB;               // rows per 1 KiB DMA
+  constexpr int NCB = D / COLS;                // column blocks per head
+  constexpr int NDT = COLS / 64;               // 16-column blocks per wave
   extern __shared__ uint4 smem[];
   lds_u8* const sb = (lds_u8*)smem;
   const uint32_t lds0 = (uint32_t)(uintptr_t)sb;
@@ -1060,22 +1070,30 @@ __global__ __launch_bounds__(kThreads) void absorb_q_kernel(const uint16_t* __re
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, i16 = lane & 15;
   const int tiles = (BT + kAbsorbRows - 1) / kAbsorbRows;
-  const int items = H * tiles;
-  const int per = (items + mla::kNumXCDs - 1) / mla::kNumXCDs;   // items per XCD slot run
+  const int items = H * tiles * NCB;
+  const int per = (items + mla::kNumXCDs - 1) / mla::kNumXCDs;   // items per XCD
   const int item = (blockIdx.x % mla::kNumXCDs) * per + blockIdx.x / mla::kNumXCDs;
   if (item >= items) return;
-  const int h = item / tiles;
-  const int row0 = (item % tiles) * kAbsorbRows;
+  const int cb = item % NCB;
+  const int h = item / NCB / tiles;
+  const int row0 = (item / NCB % tiles) * kAbsorbRows;
 
-  // ---- W_UK[h] -> LDS: row d = w + 4 i, chunk order swizzled by d & 15
+  // ---- W_UK[h][:, COLS cb .. +COLS-1] -> LDS.  DMA k moves rows RPD k ..
+  // +RPD-1; wave w issues k = w + 4 i.  Lane l fetches chunk l % (64 / RPD)
+  // of row RPD k + l / (64 / RPD), swizzled by that row's d & 15, which
+  // depends on i only through i & 3.
   const uint16_t* wh = w_uk + (size_t)h * DV * D;
-  uint32_t dvoff[4];
+  constexpr int LPR = 64 / RPD;                // lanes per staged row
+  const int lr = lane / LPR, lc = lane % LPR;  // row within the DMA, 16-byte chunk within the row
+  uint32_t voff[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) dvoff[j] = 16u * (uint32_t)(lane ^ swz16((w + 4 * j) & 15));
+  for (int j = 0; j < 4; ++j)
+    voff[j] = (uint32_t)(lr * (D * 2) + cb * RB +
+                         16 * ((lc & ~15) | ((lc & 15) ^ swz16((RPD * (w + 4 * j) + lr) & 15))));
 #pragma unroll 8
-  for (int i = 0; i < DV / 4; ++i) {
-    const int d = w + 4 * i;
-    dma_row16(wh + (size_t)d * D, dvoff[i & 3], lds0 + (uint32_t)d * 1024u);
+  for (int i = 0; i < DV / (4 * RPD); ++i) {
+    const int k = w + 4 * i;
+    dma_row16(wh + (size_t)(RPD * k) * D, voff[i & 3], lds0 + (uint32_t)k * 1024u);
   }
   // ---- q_nope^T operands of the tile, from memory meanwhile:
   // qop[rb][kk] = q_nope[row 16 rb + i16][32 kk + 8 g .. +7] (zero past BT)
@@ -1103,21 +1121,21 @@ __global__ __launch_bounds__(kThreads) void absorb_q_kernel(const uint16_t* __re
       const int k32 = 8 * g + q + 4 * hi;
       const int sv = swz16(k32 & 15);
       tsw[hi] = sv >> 1;
-      trow[hi] = (uint32_t)(k32 * 1024 + 16 * ((e4 >> 1) ^ (sv & 1)) + 8 * (e4 & 1));
+      trow[hi] = (uint32_t)(k32 * RB + 16 * ((e4 >> 1) ^ (sv & 1)) + 8 * (e4 & 1));
     }
   }
-  f32x4 acc[8][4];
+  f32x4 acc[NDT][4];
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt)
+  for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) acc[dt][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) {
-    const int c16 = 8 * w + dt;   // 16-column block of the output
+  for (int dt = 0; dt < NDT; ++dt) {
+    const int c16 = NDT * w + dt;   // 16-column block within the staged block
     bf16x8 wop[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const uint32_t base = 32768u * kk + 256u * (uint32_t)(c16 >> 3);
+      const uint32_t base = (uint32_t)(32 * RB) * kk + 256u * (uint32_t)(c16 >> 3);
       const uint32_t o0 = base + trow[0] + 32u * (uint32_t)((c16 & 7) ^ tsw[0]);
       const uint32_t o1 = base + trow[1] + 32u * (uint32_t)((c16 & 7) ^ tsw[1]);
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sb + o0));
@@ -1130,14 +1148,14 @@ __global__ __launch_bounds__(kThreads) void absorb_q_kernel(const uint16_t* __re
       for (int kk = 0; kk < 4; ++kk)
         acc[dt][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wop[kk], qop[rb][kk], acc[dt][rb], 0, 0, 0);
   }
-  // ---- acc[dt][rb][i] = q_lat[row 16 rb + i16][col 128 w + 16 dt + 4 g + i]
+  // ---- acc[dt][rb][i] = q_lat[row 16 rb + i16][col COLS cb + 16 (NDT w + dt) + 4 g + i]
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
     const int row = row0 + 16 * rb + i16;
     if (row >= BT) continue;
-    uint16_t* dst = q_lat + ((size_t)row * H + h) * D + 128 * w + 4 * g;
+    uint16_t* dst = q_lat + ((size_t)row * H + h) * D + COLS * cb + 16 * NDT * w + 4 * g;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
+    for (int dt = 0; dt < NDT; ++dt) {
       const f32x4 v = acc[dt][rb];
       *reinterpret_cast<u32x2*>(dst + 16 * dt) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
     }
@@ -1165,8 +1183,8 @@ int ensure_device() {
       for (const void* f : attn)
         fail |= hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kAttnSmemBytes) !=
                 hipSuccess;
-      fail |= hipFuncSetAttribute(reinterpret_cast<const void*>(absorb_q_kernel),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, kAbsorbSmemBytes) != hipSuccess;
+      fail |= hipFuncSetAttribute(reinterpret_cast<const void*>(absorb_q_kernel<512>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, DV * 512 * 2) != hipSuccess;
       if (fail)
         return MLA_ERR_HIP;
     }
@@ -1339,10 +1357,18 @@ int mla_verify_absorb_q(const mla_verify_params* p, const mla_bf16* q_nope, cons
   rc = ensure_device();
   if (rc != MLA_OK) return rc;
   const int bt_rows = p->batch * p->q_len;
-  const int items = ((bt_rows + kAbsorbRows - 1) / kAbsorbRows) * p->num_heads;
+  // whole rows of W_UK[h] per workgroup once the (head, tile) items fill the
+  // GPU; column quarters for a small batch
+  const int pairs = ((bt_rows + kAbsorbRows - 1) / kAbsorbRows) * p->num_heads;
+  const bool whole = pairs >= mla::kNumCUs;
+  const int items = pairs * (whole ? 1 : 4);
   const unsigned grid = (unsigned)((items + mla::kNumXCDs - 1) / mla::kNumXCDs * mla::kNumXCDs);
-  hipLaunchKernelGGL(absorb_q_kernel, dim3(grid), dim3(kThreads), kAbsorbSmemBytes,
-                     static_cast<hipStream_t>(stream), q_nope, w_uk, q_latent, bt_rows, p->num_heads);
+  if (whole)
+    hipLaunchKernelGGL(absorb_q_kernel<512>, dim3(grid), dim3(kThreads), DV * 512 * 2,
+                       static_cast<hipStream_t>(stream), q_nope, w_uk, q_latent, bt_rows, p->num_heads);
+  else
+    hipLaunchKernelGGL(absorb_q_kernel<128>, dim3(grid), dim3(kThreads), DV * 128 * 2,
+                       static_cast<hipStream_t>(stream), q_nope, w_uk, q_latent, bt_rows, p->num_heads);
   return launch_status();
 }
 

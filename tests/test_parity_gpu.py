@@ -238,6 +238,28 @@ def test_gated_parity(cfg, splits, tile):
     check_gated(x, d, q_bits, num_splits=splits, what=f"cfg{cfg}", tile_rows=tile)
 
 
+@pytest.mark.parametrize("batch,q_len,heads", [(5, 14, 3), (13, 10, 128)])
+def test_absorb_q_ragged_tiles(batch, q_len, heads):
+    """Row counts that leave a partial 64-row tile, on both column blockings
+    (quarters for a small batch, whole rows once the (head, tile) pairs fill
+    the GPU: 3 tiles x 128 heads)."""
+    log(f"absorb: B={batch} T={q_len} H={heads}")
+    x = build_inputs(batch=batch, heads=heads, q_len=q_len, ctx=np.full(batch, 40), seed=31)
+    d = upload(x)
+    got = bits_of(mv.verify_absorb_q(d["q_nope"], d["w_uk"]))
+    sync()
+    want = oracle.absorb_query(x.q_nope, x.w_uk)
+    # fp32 sum then one bf16 rounding: within half a bf16 ulp plus the fp32
+    # summation bound n * 2^-24 * sum|q_d W_dc| of the float64 value
+    g = oracle.bf16_to_f64(got)
+    mag = np.einsum("bthd,hdc->bthc", np.abs(oracle.bf16_to_f64(x.q_nope)),
+                    np.abs(oracle.bf16_to_f64(x.w_uk)))
+    top = np.maximum(np.abs(g), np.abs(want))
+    ulp = np.exp2(np.floor(np.log2(np.maximum(top, 1e-38))) - 7)
+    excess = np.abs(g - want) - (0.5 * ulp + 128 * 2.0 ** -24 * mag)
+    assert np.all(excess <= 0), float(excess.max())
+
+
 # ------------------------------------------------------------------ end to end
 @pytest.mark.parametrize("cfg", [1, 2])
 def test_end_to_end_against_unabsorbed_oracle(cfg):
