@@ -235,6 +235,8 @@ def main():
                     help="force rows per attention workgroup (0 = library)")
     ap.add_argument("--eager", action="store_true", help="time eager launches, not graph replay")
     ap.add_argument("--warm", action="store_true", help="one pool copy (cache-warm)")
+    ap.add_argument("--noncausal", action="store_true",
+                    help="every token of a group sees the group's largest bound (draft-block fold)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
@@ -271,6 +273,8 @@ def main():
         del src, dst
 
     x = make_config(args.config)
+    if args.noncausal:
+        x.kv_bounds[:] = x.kv_bounds.max(axis=1, keepdims=True)
     b, t, h = x.shape
     gated = x.gated
     splits = x.num_splits if args.splits is None else args.splits
@@ -425,6 +429,7 @@ def main():
         "config": {"workload": WORKLOAD_NAMES[args.config], "batch": b, "heads": h, "q_len": t,
                    "num_splits": s_used, "tile_rows": tile_used, "gated": gated,
                    "cache": "warm" if args.warm else f"cold: {n_sets} rotating pool copies",
+                   "bounds": "non-causal (group max)" if args.noncausal else "causal per token",
                    "launch": mode},
         "roofline": roof,
         "extra": {"attention_kernel_us": round(kms * 1e3, 3),

@@ -121,6 +121,22 @@ def test_fold_shapes(heads, q_len):
                          what=f"H{heads}T{q_len}S{s}tile{tile}")
 
 
+@pytest.mark.parametrize("heads,q_len", [(8, 8), (64, 8), (64, 1)])
+def test_noncausal_draft_block_equal_bounds(heads, q_len):
+    """The drafter's own attention: every token of a group shares
+    one bound, so masking is needed only in a request's last page.  Lengths
+    land on, just before and just after page boundaries; one request sees
+    nothing."""
+    log(f"non-causal draft block H={heads} T={q_len}")
+    ctx = np.array([1024, 1023, 1025, 64, 1, 0, 700, 1536])
+    bounds = np.repeat(ctx[:, None], q_len, axis=1).astype(np.int32)
+    x = build_inputs(batch=len(ctx), heads=heads, q_len=q_len, ctx=ctx, bounds=bounds, seed=33,
+                     latent_q=True, q_scale=1536.0)
+    d = upload(x)
+    for s in (0, 1, 3):
+        check_latent(x, d, x.q_latent, num_splits=s, what=f"equal bounds S{s}")
+
+
 def test_random_bounds_zero_rows_and_empty_requests():
     log("random bounds incl. zero rows, an all-zero request, bounds past the table")
     rng = np.random.default_rng(5)
