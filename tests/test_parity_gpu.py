@@ -121,6 +121,25 @@ def test_fold_shapes(heads, q_len):
                          what=f"H{heads}T{q_len}S{s}tile{tile}")
 
 
+def test_long_context_block_table_past_one_split_staging():
+    """A block-table row longer than one split stages in LDS (1024 page ids):
+    each split then loads only its own slice of the row.  70000 keys = 1094
+    pages; the library's split count, a forced 2 (547 pages per split) and 3,
+    and the rejection of a forced single split (1094 > 1024 pages)."""
+    log("long context: B=2 ctx=(70000, 3000) H=8 T=4")
+    q_len = 4
+    ctx = np.array([70000, 3000])
+    x = build_inputs(batch=2, heads=8, q_len=q_len, ctx=ctx, seed=41, latent_q=True, q_scale=1536.0)
+    assert x.block_table.shape[1] > 1024
+    d = upload(x)
+    for s in (0, 2, 3):
+        check_latent(x, d, x.q_latent, num_splits=s, what=f"long S{s}")
+    with pytest.raises(mv.MlaVerifyError) as e:
+        mv.verify_attn(d["q_latent"], d["pool"], d["block_table"], d["kv_bounds"], x.sm_scale,
+                       num_splits=1)
+    assert e.value.code == -4
+
+
 @pytest.mark.parametrize("heads,q_len", [(8, 8), (64, 8), (64, 1)])
 def test_noncausal_draft_block_equal_bounds(heads, q_len):
     """The drafter's own attention: every token of a group shares
