@@ -53,6 +53,39 @@ def bf16_to_f64(bits) -> np.ndarray:
     return (u << np.uint32(16)).view(np.float32).astype(np.float64)
 
 
+def fp8_e4m3_to_f64(codes) -> np.ndarray:
+    """Decode OCP FP8 E4M3 codes (uint8) exactly into float64.
+
+    Bit fields, most significant first: sign (1), exponent (4, bias 7),
+    mantissa (3).  Exponent field 0 is subnormal: (m / 8) * 2^-6.  Otherwise
+    the value is (1 + m / 8) * 2^(e - 7).  The format has no infinities: only
+    the all-ones exponent with all-ones mantissa (0x7F, 0xFF) is NaN, so
+    0x7E = 1.75 * 2^8 = 448 is the largest finite value.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where((c >> 7) & 1, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    out = sign * mag
+    return np.where((c & 0x7F) == 0x7F, np.nan, out)
+
+
+def kv_decoder(kv_dtype: str = "bf16", kv_scale: float = 1.0):
+    """The function that turns stored latent-cache elements into float64.
+
+    bf16: the exact value of each bit pattern.  fp8 (E4M3): kv_scale times the
+    exact value of each code (one scale for the whole cache; the latent serves
+    as key and as value, so both uses see the same scaled value).
+    """
+    if kv_dtype == "bf16":
+        return bf16_to_f64
+    if kv_dtype == "fp8":
+        scale = float(kv_scale)
+        return lambda codes: fp8_e4m3_to_f64(codes) * scale
+    raise ValueError(kv_dtype)
+
+
 def sigmoid(x) -> np.ndarray:
     """1 / (1 + e^-x) in float64, evaluated without overflow."""
     x = np.asarray(x, dtype=np.float64)
@@ -65,14 +98,16 @@ def sigmoid(x) -> np.ndarray:
 
 
 # ----------------------------------------------------------------- paging
-def request_keys(pool, block_table, kv_bounds, b) -> tuple[np.ndarray, int]:
+def request_keys(pool, block_table, kv_bounds, b, decode=None) -> tuple[np.ndarray, int]:
     """The latent cache rows request b can see, in logical order.
 
     Logical token j of request b lives in page block_table[b, j // 64] at slot
     j % 64.  Only the first n_b = max_t bound tokens are gathered, so pages
-    past ceil(n_b / 64) and slots past n_b are never read.
+    past ceil(n_b / 64) and slots past n_b are never read.  ``decode`` turns
+    the stored elements into float64 (default: bf16 bit patterns).
     Returns (C_b [n_b, 512] float64, n_b).
     """
+    decode = bf16_to_f64 if decode is None else decode
     max_pages = block_table.shape[1]
     n_b = int(np.clip(np.max(kv_bounds[b]), 0, max_pages * PAGE))
     if n_b == 0:
@@ -80,7 +115,7 @@ def request_keys(pool, block_table, kv_bounds, b) -> tuple[np.ndarray, int]:
     n_pages = -(-n_b // PAGE)
     pages = pool[np.asarray(block_table[b, :n_pages], dtype=np.int64)]
     rows = np.asarray(pages).reshape(n_pages * PAGE, LATENT)[:n_b]
-    return bf16_to_f64(rows), n_b
+    return decode(rows), n_b
 
 
 def token_bound(kv_bounds, b, t, n_b) -> int:
@@ -119,21 +154,24 @@ def absorb_query(q_nope, w_uk) -> np.ndarray:
 
 
 def verify_attention_latent(q_latent, pool, block_table, kv_bounds, sm_scale,
-                            q_is_f64: bool = False):
+                            q_is_f64: bool = False, kv_dtype: str = "bf16", kv_scale: float = 1.0):
     """The latent-space (absorbed) definition the C-ABI computes.
 
     For every request b, token t, head h with bound L = kv_bounds[b, t]:
       s_j   = sm_scale * <q_latent[b,t,h], C_b[j]>       for j < L
       lse   = log sum_j exp(s_j)                         (-inf when L = 0)
       o_lat = sum_j softmax(s)_j C_b[j]                  (0 when L = 0)
+    C_b holds the decoded cache rows (``kv_decoder``: bf16, or fp8 E4M3 codes
+    times kv_scale).
     Returns (o_lat [B,T,H,512] float64, lse [B,T,H] float64).
     """
     q = q_latent if q_is_f64 else bf16_to_f64(q_latent)
+    decode = kv_decoder(kv_dtype, kv_scale)
     bsz, tlen, heads, _ = q.shape
     o = np.zeros((bsz, tlen, heads, LATENT))
     lse = np.full((bsz, tlen, heads), -np.inf)
     for b in range(bsz):
-        c_b, n_b = request_keys(pool, block_table, kv_bounds, b)
+        c_b, n_b = request_keys(pool, block_table, kv_bounds, b, decode)
         for t in range(tlen):
             L = token_bound(kv_bounds, b, t, n_b)
             if L == 0:
@@ -144,7 +182,7 @@ def verify_attention_latent(q_latent, pool, block_table, kv_bounds, sm_scale,
 
 
 def verify_attention_mla(q_nope, w_uk, w_uv, gate, pool, block_table, kv_bounds, sm_scale,
-                         requests=None):
+                         requests=None, kv_dtype: str = "bf16", kv_scale: float = 1.0):
     """Unabsorbed gated NoPE MLA over the paged latent cache (primary definition).
 
     Per request b and head h the latent rows are up-projected explicitly:
@@ -155,9 +193,11 @@ def verify_attention_mla(q_nope, w_uk, w_uv, gate, pool, block_table, kv_bounds,
       o_lat = sum_j softmax(s)_j C_b[j]                        [512]
       out   = sigmoid(gate[b,t,h]) * o_v                       [128]
     with the (-inf, 0) identity for L = 0.  ``requests`` restricts the work to
-    a subset of b (other entries stay at the identity / NaN-free zeros).
+    a subset of b (other entries stay at the identity / NaN-free zeros).  The
+    cache rows C_b are decoded by ``kv_decoder(kv_dtype, kv_scale)``.
     Returns a dict with o_v, o_lat, lse, out (float64).
     """
+    decode = kv_decoder(kv_dtype, kv_scale)
     qn = bf16_to_f64(q_nope)
     wk = bf16_to_f64(w_uk)
     wv = bf16_to_f64(w_uv)
@@ -169,7 +209,7 @@ def verify_attention_mla(q_nope, w_uk, w_uv, gate, pool, block_table, kv_bounds,
         "lse": np.full((bsz, tlen, heads), -np.inf),
     }
     for b in (range(bsz) if requests is None else requests):
-        c_b, n_b = request_keys(pool, block_table, kv_bounds, b)
+        c_b, n_b = request_keys(pool, block_table, kv_bounds, b, decode)
         for h in range(heads):
             k_h = c_b @ wk[h].T
             v_h = c_b @ wv[h].T

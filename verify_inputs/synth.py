@@ -40,6 +40,12 @@ LATENT = 512          # latent rank of the compressed KV
 PAGE = 64             # tokens per KV page
 NOPE = 128            # per-head q_nope / value dim
 BF16_NAN = np.uint16(0x7FC0)
+FP8_NAN = np.uint8(0x7F)      # OCP E4M3 NaN code
+# Scale of the fp8 cache workloads: latent = FP8_KV_SCALE * E4M3 value.  A
+# power of two, so dividing the bf16 draws by it is exact; the draws (std
+# 1/sqrt(512) ~ 0.044) then sit at codes of magnitude ~11 (E4M3 covers up to
+# 448), far above the subnormal range.
+FP8_KV_SCALE = 2.0 ** -8
 
 CONFIG_SEEDS = {1: 0, 2: 1, 3: 2, 4: 3, 5: 4}
 
@@ -82,6 +88,8 @@ class VerifyInputs:
     num_splits: int
     gated: bool
     q_latent: np.ndarray | None = None   # [B, T, H, 512] bf16, direct draw
+    kv_dtype: str = "bf16"               # "bf16", or "fp8" (pool holds E4M3 codes)
+    kv_scale: float = 1.0                # fp8: latent = kv_scale * code value
 
     @property
     def shape(self):
@@ -90,9 +98,10 @@ class VerifyInputs:
 
 
 class SparsePool:
-    """A [num_pages, 64, 512] bf16 page pool of which only referenced pages are
+    """A [num_pages, 64, 512] page pool of which only referenced pages are
     stored; every other page reads as NaN.  Indexing with an integer page-id
-    array returns the dense pages, like a numpy array would."""
+    array returns the dense pages, like a numpy array would.  Elements are
+    bf16 bit patterns (uint16) or, for an fp8 cache, E4M3 codes (uint8)."""
 
     def __init__(self, num_pages: int, page_ids: np.ndarray, pages: np.ndarray):
         self.num_pages = int(num_pages)
@@ -101,20 +110,21 @@ class SparsePool:
         self.slot = np.full(self.num_pages, -1, dtype=np.int64)
         self.slot[self.page_ids] = np.arange(self.page_ids.size)
         self.shape = (self.num_pages, PAGE, LATENT)
-        self.dtype = np.dtype(np.uint16)
+        self.dtype = np.dtype(pages.dtype)
+        self.fill = FP8_NAN if self.dtype == np.uint8 else BF16_NAN
 
     def __getitem__(self, idx):
         idx = np.asarray(idx, dtype=np.int64)
         if np.any((idx < 0) | (idx >= self.num_pages)):
             raise IndexError("page id outside the pool")
         s = self.slot[idx]
-        out = np.full(idx.shape + (PAGE, LATENT), BF16_NAN, dtype=np.uint16)
+        out = np.full(idx.shape + (PAGE, LATENT), self.fill, dtype=self.dtype)
         have = s >= 0
         out[have] = self.pages[s[have]]
         return out
 
     def dense(self) -> np.ndarray:
-        out = np.full(self.shape, BF16_NAN, dtype=np.uint16)
+        out = np.full(self.shape, self.fill, dtype=self.dtype)
         out[self.page_ids] = self.pages
         return out
 
@@ -273,10 +283,38 @@ def make_config(n: int, seed: int | None = None, *, sharp: bool = False,
                    permute_single=(spec.ctx == "fixed256"))
 
 
+def bf16_bits_to_fp8_codes(bits, kv_scale: float) -> np.ndarray:
+    """E4M3 codes of bf16 values divided by ``kv_scale``: round to nearest
+    even, NaN stays NaN (code 0x7F).  The encoding is torch's float8_e4m3fn
+    conversion on the CPU; values are clipped to +-448 first so nothing maps
+    to NaN by overflow.  (Input plumbing: it writes the cache an fp8 serving
+    stack would hold; the attention reads the codes.)"""
+    import torch
+
+    x = bf16_bits_to_f32(bits).astype(np.float64) / float(kv_scale)
+    nan = np.isnan(x)
+    x = np.clip(np.where(nan, 0.0, x), -448.0, 448.0).astype(np.float32)
+    codes = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    codes[nan] = FP8_NAN
+    return codes
+
+
+def fp8_cache(inp: VerifyInputs, kv_scale: float = FP8_KV_SCALE) -> VerifyInputs:
+    """The same verify batch with its latent cache stored as fp8 E4M3 codes
+    (``kv_scale`` times the code's value approximates each bf16 latent).
+    Unreferenced pages and slots past the last visible key stay NaN."""
+    pool = inp.pool
+    pages = bf16_bits_to_fp8_codes(pool.pages, kv_scale)
+    out = dataclasses.replace(inp, pool=SparsePool(pool.num_pages, pool.page_ids, pages))
+    out.kv_dtype, out.kv_scale = "fp8", float(kv_scale)
+    return out
+
+
 def referenced_kv_bytes(inp: VerifyInputs) -> int:
-    """Bytes of KV a kernel must read: 1 KiB per visible key of each request."""
+    """Bytes of KV a kernel must read: one latent row (1 KiB in bf16, 512 B in
+    fp8) per visible key of each request."""
     n = np.clip(inp.kv_bounds.max(axis=1), 0, inp.block_table.shape[1] * PAGE)
-    return int(n.sum()) * LATENT * 2
+    return int(n.sum()) * LATENT * (1 if inp.kv_dtype == "fp8" else 2)
 
 
 @dataclasses.dataclass
