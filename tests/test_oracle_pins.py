@@ -372,11 +372,11 @@ def test_planted_oracle_mistakes_are_caught(monkeypatch, mutant):
     elif mutant == "page_reversed":
         orig = om.request_keys
 
-        def rk(pool, bt, kb, b):
+        def rk(pool, bt, kb, b, decode=None):
             n_pg = -(-int(np.clip(np.max(kb[b]), 0, bt.shape[1] * PAGE)) // PAGE)
             bt2 = bt.copy()
             bt2[b, :n_pg] = bt[b, :n_pg][::-1]
-            return orig(pool, bt2, kb, b)
+            return orig(pool, bt2, kb, b, decode)
         monkeypatch.setattr(om, "request_keys", rk)
     elif mutant == "scores_perturbed":
         orig = om.softmax_attend
