@@ -33,12 +33,22 @@
  *     lse    = ln sum_j exp(s_j)                    (-inf if L == 0)
  *     o_lat  = sum_j softmax(s)_j C_b[j,:]          (0    if L == 0)
  *     out    = sigmoid(gate[b,t,h,:]) * (W_UV[h] o_lat)   (gated entry)
- * where C_b[j] = latent_kv_pages[block_table[b, j/64], j%64, :].
+ * where C_b[j] = latent_kv_pages[block_table[b, j/64], j%64, :], or, for an
+ * fp8 cache, kv_scale times the value of that E4M3 code.
+ *
+ * fp8 latent cache (kv_dtype = MLA_KV_FP8_E4M3).  The first page serves with
+ * an fp8 KV cache ("--kv-cache-dtype fp8" in its launch command), and the
+ * Helix page notes that its per-token-bound decode kernel still rejects fp8
+ * KV.  Neither fixes the encoding, so this library reads it as OCP FP8 E4M3
+ * (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no infinities;
+ * 0x7F / 0xFF are NaN) with one scale per cache: a latent element is
+ * kv_scale * value(code), for its use as key and as value alike.  Queries,
+ * softmax weights and outputs stay as in the bf16 path.
  *
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers, row-major, contiguous, with
  *    the shapes given below, and 16-byte aligned.  bf16 is stored as its
- *    16-bit pattern (mla_bf16).
+ *    16-bit pattern (mla_bf16), fp8 as its 8-bit code.
  *  - The caller owns every buffer and the stream.  The library never
  *    allocates, frees or keeps a pointer after it returns; inputs are
  *    read-only; outputs are fully overwritten (masked rows get 0 / -inf).
@@ -73,7 +83,8 @@ enum mla_verify_status {
   MLA_OK = 0,
   MLA_ERR_NULL = -1,        /* a required pointer is NULL                  */
   MLA_ERR_SHAPE = -2,       /* latent != 512, page != 64, T/H/B out of range */
-  MLA_ERR_DTYPE = -3,       /* kv_dtype other than MLA_KV_BF16 (fp8 etc.)  */
+  MLA_ERR_DTYPE = -3,       /* kv_dtype not MLA_KV_BF16 / MLA_KV_FP8_E4M3, */
+                            /* or fp8 where the entry point takes bf16 only */
   MLA_ERR_ARG = -4,         /* bad sm_scale, num_splits, pool size, or a   */
                             /* pointer that is not 16-byte aligned         */
   MLA_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required  */
@@ -83,7 +94,7 @@ enum mla_verify_status {
 
 enum mla_verify_kv_dtype {
   MLA_KV_BF16 = 0,
-  MLA_KV_FP8_E4M3 = 1       /* declared so callers can ask; always rejected */
+  MLA_KV_FP8_E4M3 = 1       /* OCP FP8 E4M3 codes times kv_scale           */
 };
 
 /* Limits (MLA_ERR_SHAPE outside them). */
@@ -104,9 +115,12 @@ typedef struct mla_verify_params {
   int32_t num_pool_pages;    /* N, pages in latent_kv_pages (>= 1)           */
   int32_t num_splits;        /* 0 = library's choice; 1..64 = forced split-KV */
   float sm_scale;            /* softmax scale, finite and > 0                */
-  int32_t kv_dtype;          /* MLA_KV_BF16 only                             */
+  int32_t kv_dtype;          /* MLA_KV_BF16 or MLA_KV_FP8_E4M3 (attention
+                                entry points; the cache updates take bf16)  */
   int32_t tile_rows;         /* 0 = library's choice; 32, 64 or 128 = forced
                                 folded rows per attention workgroup          */
+  float kv_scale;            /* fp8 cache: latent = kv_scale * value(code),
+                                finite and > 0; ignored for bf16            */
 } mla_verify_params;
 
 /* Validates `p` (pure host code, no HIP call).  MLA_OK or an error code. */
@@ -129,7 +143,9 @@ int mla_verify_workspace_size(const mla_verify_params* p, int gated, size_t* byt
 
 /* Verify attention, latent output.
  *   q_latent        [B, T, H, 512] bf16   absorbed queries (row t*H+h = fold)
- *   latent_kv_pages [N, 64, 512]   bf16   paged latent cache
+ *   latent_kv_pages [N, 64, 512]   bf16   paged latent cache (fp8 E4M3
+ *                                         codes, 512 B per key row, when
+ *                                         kv_dtype is MLA_KV_FP8_E4M3)
  *   block_table     [B, P]         int32  page ids in logical order
  *   kv_bounds       [B, T]         int32  visible-key count per token
  *   out_latent      [B, T, H, 512] bf16   o_lat (0 for rows with bound 0)
@@ -139,7 +155,7 @@ int mla_verify_workspace_size(const mla_verify_params* p, int gated, size_t* byt
  * MLA_ERR_HIP (launch failure, reported without synchronising). */
 int mla_verify_attn(const mla_verify_params* p,
                     const mla_bf16* q_latent,
-                    const mla_bf16* latent_kv_pages,
+                    const void* latent_kv_pages,
                     const int32_t* block_table,
                     const int32_t* kv_bounds,
                     mla_bf16* out_latent,
@@ -165,7 +181,7 @@ int mla_verify_attn(const mla_verify_params* p,
  * (mla_verify_lse_combine).  Errors as mla_verify_attn. */
 int mla_verify_attn_partials(const mla_verify_params* p,
                              const mla_bf16* q_latent,
-                             const mla_bf16* latent_kv_pages,
+                             const void* latent_kv_pages,
                              const int32_t* block_table,
                              const int32_t* kv_bounds,
                              mla_bf16* part_o,
@@ -198,7 +214,7 @@ int mla_verify_lse_combine(int num_splits, int rows,
  * Other arguments and errors as mla_verify_attn. */
 int mla_verify_attn_gated(const mla_verify_params* p,
                           const mla_bf16* q_latent,
-                          const mla_bf16* latent_kv_pages,
+                          const void* latent_kv_pages,
                           const int32_t* block_table,
                           const int32_t* kv_bounds,
                           const mla_bf16* w_uv,

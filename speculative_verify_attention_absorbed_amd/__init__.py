@@ -62,15 +62,16 @@ class VerifyParams(ctypes.Structure):
         ("latent_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
         ("max_pages_per_req", ctypes.c_int32), ("num_pool_pages", ctypes.c_int32),
         ("num_splits", ctypes.c_int32), ("sm_scale", ctypes.c_float), ("kv_dtype", ctypes.c_int32),
-        ("tile_rows", ctypes.c_int32),
+        ("tile_rows", ctypes.c_int32), ("kv_scale", ctypes.c_float),
     ]
 
     @classmethod
     def make(cls, batch, q_len, num_heads, max_pages_per_req, num_pool_pages, sm_scale,
-             num_splits=0, latent_dim=LATENT, page_size=PAGE, kv_dtype=KV_BF16, tile_rows=0):
+             num_splits=0, latent_dim=LATENT, page_size=PAGE, kv_dtype=KV_BF16, tile_rows=0,
+             kv_scale=1.0):
         return cls(int(batch), int(q_len), int(num_heads), int(latent_dim), int(page_size),
                    int(max_pages_per_req), int(num_pool_pages), int(num_splits), float(sm_scale),
-                   int(kv_dtype), int(tile_rows))
+                   int(kv_dtype), int(tile_rows), float(kv_scale))
 
 
 _LIB = None
@@ -191,11 +192,20 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
-def _params_from(q_latent, pool, block_table, sm_scale, num_splits, kv_dtype, tile_rows=0):
+def _params_from(q_latent, pool, block_table, sm_scale, num_splits, kv_dtype, tile_rows=0,
+                 kv_scale=1.0):
     b, t, h, d = q_latent.shape
     return VerifyParams.make(b, t, h, block_table.shape[1], pool.shape[0], sm_scale, num_splits,
                              latent_dim=d, page_size=pool.shape[1] if pool.dim() == 3 else PAGE,
-                             kv_dtype=kv_dtype, tile_rows=tile_rows)
+                             kv_dtype=kv_dtype, tile_rows=tile_rows, kv_scale=kv_scale)
+
+
+def _pool_types(kv_dtype):
+    """Element types accepted for the latent cache: bf16, or 8-bit codes."""
+    torch = _torch()
+    if int(kv_dtype) == KV_FP8_E4M3:
+        return tuple(t for t in (torch.uint8, getattr(torch, "float8_e4m3fn", None)) if t is not None)
+    return _bf16_types()
 
 
 def _workspace(params, gated, workspace, device):
@@ -213,18 +223,19 @@ def _workspace(params, gated, workspace, device):
 
 def verify_attn(q_latent, latent_kv_pages, block_table, kv_bounds, sm_scale, *, num_splits=0,
                 out_latent=None, lse=None, workspace=None, stream=None, kv_dtype=KV_BF16,
-                tile_rows=0):
+                tile_rows=0, kv_scale=1.0):
     """``mla_verify_attn``: returns (out_latent, lse).  Outputs and workspace are
     allocated with torch when not given (allocation happens here, outside the
     library)."""
     torch = _torch()
     params = _params_from(q_latent, latent_kv_pages, block_table, sm_scale, num_splits, kv_dtype,
-                          tile_rows)
+                          tile_rows, kv_scale)
     _check(verify_check(params), "mla_verify_attn")
     b, t, h, d = q_latent.shape
     bf = _bf16_types()
     _dev_tensor(q_latent, "q_latent", (b, t, h, LATENT), bf)
-    _dev_tensor(latent_kv_pages, "latent_kv_pages", (latent_kv_pages.shape[0], PAGE, LATENT), bf)
+    _dev_tensor(latent_kv_pages, "latent_kv_pages", (latent_kv_pages.shape[0], PAGE, LATENT),
+                _pool_types(kv_dtype))
     _dev_tensor(block_table, "block_table", (b, block_table.shape[1]), (torch.int32,))
     _dev_tensor(kv_bounds, "kv_bounds", (b, t), (torch.int32,))
     dev = q_latent.device
@@ -246,16 +257,17 @@ def verify_attn(q_latent, latent_kv_pages, block_table, kv_bounds, sm_scale, *, 
 def verify_attn_gated(q_latent, latent_kv_pages, block_table, kv_bounds, w_uv, gate_logits,
                       sm_scale, *, num_splits=0, out=None, lse=None, out_latent=None,
                       want_latent=False, workspace=None, stream=None, kv_dtype=KV_BF16,
-                      tile_rows=0):
+                      tile_rows=0, kv_scale=1.0):
     """``mla_verify_attn_gated``: returns (out, lse, out_latent or None)."""
     torch = _torch()
     params = _params_from(q_latent, latent_kv_pages, block_table, sm_scale, num_splits, kv_dtype,
-                          tile_rows)
+                          tile_rows, kv_scale)
     _check(verify_check(params), "mla_verify_attn_gated")
     b, t, h, d = q_latent.shape
     bf = _bf16_types()
     _dev_tensor(q_latent, "q_latent", (b, t, h, LATENT), bf)
-    _dev_tensor(latent_kv_pages, "latent_kv_pages", (latent_kv_pages.shape[0], PAGE, LATENT), bf)
+    _dev_tensor(latent_kv_pages, "latent_kv_pages", (latent_kv_pages.shape[0], PAGE, LATENT),
+                _pool_types(kv_dtype))
     _dev_tensor(block_table, "block_table", (b, block_table.shape[1]), (torch.int32,))
     _dev_tensor(kv_bounds, "kv_bounds", (b, t), (torch.int32,))
     _dev_tensor(w_uv, "w_uv", (h, NOPE, LATENT), bf)
@@ -282,17 +294,18 @@ def verify_attn_gated(q_latent, latent_kv_pages, block_table, kv_bounds, w_uv, g
 
 def verify_attn_partials(q_latent, latent_kv_pages, block_table, kv_bounds, sm_scale, *,
                          num_splits=0, part_o=None, part_lse=None, stream=None,
-                         kv_dtype=KV_BF16, tile_rows=0):
+                         kv_dtype=KV_BF16, tile_rows=0, kv_scale=1.0):
     """``mla_verify_attn_partials``: returns (part_o [S, B*T*H, 512] bf16,
     part_lse [S, B*T*H] f32) with S = verify_num_splits(params)."""
     torch = _torch()
     params = _params_from(q_latent, latent_kv_pages, block_table, sm_scale, num_splits, kv_dtype,
-                          tile_rows)
+                          tile_rows, kv_scale)
     _check(verify_check(params), "mla_verify_attn_partials")
     b, t, h, d = q_latent.shape
     bf = _bf16_types()
     _dev_tensor(q_latent, "q_latent", (b, t, h, LATENT), bf)
-    _dev_tensor(latent_kv_pages, "latent_kv_pages", (latent_kv_pages.shape[0], PAGE, LATENT), bf)
+    _dev_tensor(latent_kv_pages, "latent_kv_pages", (latent_kv_pages.shape[0], PAGE, LATENT),
+                _pool_types(kv_dtype))
     _dev_tensor(block_table, "block_table", (b, block_table.shape[1]), (torch.int32,))
     _dev_tensor(kv_bounds, "kv_bounds", (b, t), (torch.int32,))
     s = verify_num_splits(params)

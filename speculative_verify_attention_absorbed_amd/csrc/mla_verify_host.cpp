@@ -12,7 +12,9 @@ namespace mla {
 
 int check_params(const mla_verify_params* p) {
   if (p == nullptr) return MLA_ERR_NULL;
-  if (p->kv_dtype != MLA_KV_BF16) return MLA_ERR_DTYPE;
+  if (p->kv_dtype != MLA_KV_BF16 && p->kv_dtype != MLA_KV_FP8_E4M3) return MLA_ERR_DTYPE;
+  if (p->kv_dtype == MLA_KV_FP8_E4M3 && (!std::isfinite(p->kv_scale) || !(p->kv_scale > 0.0f)))
+    return MLA_ERR_ARG;
   if (p->latent_dim != MLA_VERIFY_LATENT || p->page_size != MLA_VERIFY_PAGE) return MLA_ERR_SHAPE;
   if (p->batch < 1 || p->q_len < 1 || p->q_len > MLA_VERIFY_MAX_Q_LEN || p->num_heads < 1 ||
       p->num_heads > MLA_VERIFY_MAX_HEADS)

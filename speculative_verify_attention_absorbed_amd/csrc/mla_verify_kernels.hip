@@ -81,7 +81,7 @@ __device__ __forceinline__ int swz(int key, int c) { return key * 64 + (c ^ (key
 
 struct AttnArgs {
   const uint16_t* q;       // [B, R, 512]
-  const uint16_t* pool;    // [N, 64, 512]
+  const void* pool;        // [N, 64, 512] bf16, or fp8 E4M3 codes
   const int32_t* bt;       // [B, P]
   const int32_t* bounds;   // [B, T]
   uint16_t* out_lat;       // [B, R, 512] (direct mode)
@@ -92,6 +92,7 @@ struct AttnArgs {
   float scale_log2;        // sm_scale * log2(e)
   int direct;              // 1: write out_lat/lse, 0: write partials
   int min_split_pages;     // a split holds at least this many pages (m)
+  float kv_scale;          // fp8 cache: latent = kv_scale * code value (1 for bf16)
 };
 
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
@@ -103,6 +104,23 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) float lds_f32;
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 typedef __attribute__((ext_vector_type(8))) short s16x8;
+typedef __attribute__((ext_vector_type(2))) int i32x2;
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+
+// Eight fp8 (OCP E4M3) codes, bytes 0-3 of w0 then of w1, to eight bf16 on
+// the hardware converter (two per instruction).  Every E4M3 value is exact in
+// bf16; the cache's scale is applied in fp32 elsewhere (scores, normaliser).
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+  typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+  const bf16x4_t ab = __builtin_shufflevector(a, b, 0, 1, 2, 3);
+  const bf16x4_t cd = __builtin_shufflevector(c, d, 0, 1, 2, 3);
+  return __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
+}
 
 constexpr int kBufBytes = 128 * 1024;                           // key-row staging buffers
 constexpr int kPBytes = 10 * 1024;                              // P tile (bf16, padded rows)
@@ -250,7 +268,7 @@ __device__ __forceinline__ int logical_item(int bid, int n_groups, int row_tiles
 // one in unit 0 (the split's first key is visible whenever any is), so each
 // row's reference max is fixed there for the whole item; P may exceed 1
 // later (see kMaxJump for the second pass).
-template <int MODE>
+template <int MODE, bool KV8>
 // The arguments the prologue needs first (the work-item decode, the bounds,
 // the block table and Q) lead the list as plain scalars, so that the command
 // processor preloads them into SGPRs (the library is built with a kernarg
@@ -273,8 +291,11 @@ __global__ __launch_bounds__(256) void attn_kernel(const uint16_t* q, const int3
   constexpr int NRB = MODE == 0 ? 2 : (MODE == 1 ? 4 : 8);   // 16-row blocks of the tile
   constexpr int RT = 16 * NRB;                  // rows per tile
   constexpr int UK = KS ? 64 : 32;              // keys per staging unit
-  constexpr int NBUF = kBufBytes / (UK * 1024); // units the buffers hold
+  constexpr int ROWB = KV8 ? 512 : 1024;        // LDS bytes per staged key row
+  constexpr int UB = UK * ROWB;                 // bytes per staging unit
+  constexpr int NBUF = kBufBytes / UB < 4 ? kBufBytes / UB : 4;   // units the buffers hold
   constexpr int ROWS_PW = UK / 4;               // key rows each wave stages per unit
+  constexpr int PAIRS_PW = UK / 8;              // fp8: DMAs (two key rows each) per wave per unit
   constexpr int QKB = KS ? 1 : 2;               // 16-key blocks per wave in QK
   constexpr int QRB = KS ? NRB : 2;             // 16-row blocks per wave in QK
   constexpr int KK = UK / 32;                   // 32-key MFMA steps per unit in PV
@@ -322,12 +343,25 @@ __global__ __launch_bounds__(256) void attn_kernel(const uint16_t* q, const int3
   uint32_t dvoff[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) dvoff[j] = 16u * (uint32_t)(lane ^ swz16((w + 4 * j) & 15));
+  // fp8 key rows are 32 chunks of 16 bytes; chunk c of key k sits at chunk
+  // position c ^ (k & 15) of its LDS row (k counted from the unit's first
+  // key, a multiple of 16).  Lane l of a pair DMA writes position l & 31 of
+  // row 2 pr + (l >> 5), so it fetches that row's chunk (l & 31) ^ (k & 15);
+  // k & 15 takes two values per wave (pairs w + 4i for even and odd i).
+  uint32_t dvoff8[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int k = 2 * (w + 4 * j) + (lane >> 5);
+    dvoff8[j] = (uint32_t)((lane >> 5) * 512 + 16 * ((lane & 31) ^ (k & 15)));
+  }
 
   // ---- key-split tiles, where every wave needs every Q row, stage Q^T through
   // the last unit buffer, issued first: its address needs only the tile, so it
   // shares the memory round trip of the bounds below and is in LDS by the
   // time the first unit is issued.
-  const uint32_t qb = (uint32_t)(NBUF - 1) * (UK * 1024);
+  // (an fp8 unit is smaller than a bf16 Q tile: Q then takes the top of the
+  // staging area, and units are issued into it only after Q left)
+  const uint32_t qb = KV8 ? (uint32_t)(kBufBytes - RT * 1024) : (uint32_t)(NBUF - 1) * UB;
   if constexpr (KS) {
 #pragma unroll
     for (int i = 0; i < RT / 4; ++i) {
@@ -411,13 +445,38 @@ __global__ __launch_bounds__(256) void attn_kernel(const uint16_t* q, const int3
   // read from the pool), so 0 * garbage never reaches the PV contraction.
   // Returns the number of DMA instructions this wave issued (rows skipped
   // above issue none), which the memory-counter waits below account for.
+  // fp8: one DMA moves a pair of 512-byte key rows (2 pr, 2 pr + 1), lanes
+  // 0-31 the first; a pair that straddles the tile's extent fetches its first
+  // row with lanes 0-31 alone and zero-fills the second.
   auto issue_unit = [&](int u) {
-    const uint32_t ub = (uint32_t)(u % NBUF) * (UK * 1024);
+    const uint32_t ub = (uint32_t)(u % NBUF) * UB;
     const int kl = u * UK;                         // key offset within the split
     const int pid = __builtin_amdgcn_readfirstlane(sm_pid[pid0 + (kl >> 6)]);
     const bool pid_ok = (unsigned)pid < (unsigned)a.N;
-    const uint16_t* pbase = a.pool + ((size_t)(pid_ok ? pid : 0) * PG + (kl & 63)) * D;
     const int valid = pid_ok ? n_tile - (k_begin + kl) : 0;   // rows of the unit to fetch
+    if constexpr (KV8) {
+      const uint8_t* pbase8 = reinterpret_cast<const uint8_t*>(a.pool) +
+                              ((size_t)(pid_ok ? pid : 0) * PG + (kl & 63)) * D;
+#pragma unroll
+      for (int i = 0; i < PAIRS_PW; ++i) {
+        const int key0 = 2 * (w + 4 * i);          // first key row of the pair within the unit
+        const uint32_t dst = ub + (uint32_t)key0 * 512u;
+        if (key0 + 1 < valid) {
+          dma_row16(pbase8 + key0 * D, dvoff8[i & 1], lds0 + dst);
+        } else if (key0 < valid) {
+          if (lane < 32) dma_row16(pbase8 + key0 * D, dvoff8[i & 1], lds0 + dst);
+          else *(lds_u32x4*)(sb + dst + lane * 16) = u32x4{0u, 0u, 0u, 0u};
+        } else {
+          *(lds_u32x4*)(sb + dst + lane * 16) = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+      int ops = 0;
+#pragma unroll
+      for (int i = 0; i < PAIRS_PW; ++i) ops += 2 * (w + 4 * i) < valid;
+      return ops;
+    }
+    const uint16_t* pbase = reinterpret_cast<const uint16_t*>(a.pool) +
+                            ((size_t)(pid_ok ? pid : 0) * PG + (kl & 63)) * D;
 #pragma unroll 8
     for (int i = 0; i < ROWS_PW; ++i) {
       const int kap = w + 4 * i;                   // key row within the unit
@@ -456,6 +515,23 @@ __global__ __launch_bounds__(256) void attn_kernel(const uint16_t* q, const int3
       trow[hi] = (uint32_t)(k32 * 1024 + 16 * ((e4 >> 1) ^ (sv & 1)) + 8 * (e4 & 1));
     }
   }
+  // fp8 operands.  QK takes a k-order permuted within each pair of k-steps
+  // (2j, 2j + 1): lane g holds dims 64 j + 16 g .. +7 for step 2j and
+  // 64 j + 16 g + 8 .. +15 for step 2j + 1, one 16-byte read of its key row
+  // (chunk 4 j + g); Q^T is loaded in the same order, so the dot products
+  // are unchanged.  PV reads V^T with the 8-bit transposing read: in each
+  // 16-lane group, lane 2k + h addresses key 8g + k, dims 16 D16 + 8h .. +7,
+  // and lane i receives keys 8g .. 8g + 7 of dim 16 D16 + i.
+  const uint32_t k8row = (uint32_t)i16 * 512u;                    // K: key qkey(kb) + i16
+  const int v8key = 8 * g + (i16 >> 1);                           // V: key within a 32-key block
+  const uint32_t v8off = (uint32_t)(v8key * 512 + 8 * (i16 & 1));
+  // Q^T chunk read for k-step ks (bf16 Q rows staged with the swz16 order):
+  // chunk 8 (ks >> 1) + 2 g + (ks & 1) of row i16 sits at position chunk ^ swl
+  uint32_t q8b[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    q8b[j] = (uint32_t)(i16 * 1024 + 16 * ((8 * (j >> 1) + 2 * g + (j & 1)) ^ swl));
+
   // P tile: this lane writes rows qrow(rb), keys qkey(kb) + 4g .. +3 and reads
   // the PV B operand P[row 16 rb + i16][32 kk + 8 g .. +7]
   const uint32_t pr_off = (uint32_t)(i16 * PPITCH + 16 * g);
@@ -491,7 +567,7 @@ __global__ __launch_bounds__(256) void attn_kernel(const uint16_t* q, const int3
   };
 
   auto compute_unit = [&](int u, int pass) {
-    const uint32_t ub = (uint32_t)(u % NBUF) * (UK * 1024);
+    const uint32_t ub = (uint32_t)(u % NBUF) * UB;
     const int ukey0 = k_begin + u * UK;            // request position of the unit's first key
     // ---- S^T = K Q^T: sacc[kb][rb][i] = score(key qkey(kb) + 4g + i, row qrow(rb))
     f32x4 sacc[QKB][QRB];
@@ -502,6 +578,17 @@ __global__ __launch_bounds__(256) void attn_kernel(const uint16_t* q, const int3
     constexpr int KPG = 2;   // k-steps per operand group
     bf16x8 kop[2][KPG][QKB];
     auto load_k = [&](bf16x8 (&dst)[KPG][QKB], int grp) {
+      if constexpr (KV8) {   // one 16-byte read: k-steps 2 grp and 2 grp + 1
+        static_assert(KPG == 2, "fp8 K reads cover two k-steps");
+#pragma unroll
+        for (int kb = 0; kb < QKB; ++kb) {
+          const u32x4 x = *(const lds_u32x4*)(sb + ub + 512u * qkey(kb) + k8row +
+                                             16u * (uint32_t)((4 * grp + g) ^ i16));
+          dst[0][kb] = fp8x8_to_bf16(x[0], x[1]);
+          dst[1][kb] = fp8x8_to_bf16(x[2], x[3]);
+        }
+        return;
+      }
 #pragma unroll
       for (int e = 0; e < KPG; ++e) {
         const int ks = KPG * grp + e;
@@ -619,6 +706,15 @@ __global__ __launch_bounds__(256) void attn_kernel(const uint16_t* q, const int3
     bf16x8 vop[2][KK];
     auto load_v = [&](bf16x8 (&dst)[KK], int dt) {
       const int d16 = w * NDT + dt;
+      if constexpr (KV8) {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (lds_i32x2*)(sb + ub + 16384u * kk + v8off + 16u * (uint32_t)(d16 ^ (v8key & 15))));
+          dst[kk] = fp8x8_to_bf16((uint32_t)x[0], (uint32_t)x[1]);
+        }
+        return;
+      }
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         const uint32_t base = ub + 32768u * kk + 256u * (uint32_t)(d16 >> 3);
@@ -682,7 +778,8 @@ __global__ __launch_bounds__(256) void attn_kernel(const uint16_t* q, const int3
           const int r = min(row0 + qrow(rb), a.R - 1);
           const uint4* qp = reinterpret_cast<const uint4*>(a.q + ((size_t)b * a.R + r) * D);
 #pragma unroll
-          for (int ks = 0; ks < 16; ++ks) qreg[rb][ks] = __builtin_bit_cast(bf16x8, qp[ks * 4 + g]);
+          for (int ks = 0; ks < 16; ++ks)
+            qreg[rb][ks] = __builtin_bit_cast(bf16x8, qp[KV8 ? 8 * (ks >> 1) + 2 * g + (ks & 1) : ks * 4 + g]);
         }
       }
     }
@@ -695,14 +792,15 @@ __global__ __launch_bounds__(256) void attn_kernel(const uint16_t* q, const int3
 #pragma unroll
         for (int ks = 0; ks < 16; ++ks) {
           if (rb < 2) {
-            qreg[rb][ks] = *(const lds_bf16x8*)(sb + qb + qkb[ks & 3] + 64 * (ks & 12) + 16384 * rb);
+            qreg[rb][ks] = *(const lds_bf16x8*)(sb + qb + (KV8 ? q8b[ks & 3] : qkb[ks & 3]) + 64 * (ks & 12) +
+                                                16384 * rb);
           } else {
             // row blocks 2, 3 live in accumulation registers (the MFMA B
             // operand reads them there); load them straight in so the
             // compiler never parks them in VGPRs
             asm volatile("ds_read_b128 %0, %1 offset:%2"
                          : "=a"(qreg[rb][ks])
-                         : "v"(lds0 + qb + qkb[ks & 3]), "i"(64 * (ks & 12) + 16384 * rb)
+                         : "v"(lds0 + qb + (KV8 ? q8b[ks & 3] : qkb[ks & 3])), "i"(64 * (ks & 12) + 16384 * rb)
                          : "memory");
           }
         }
@@ -787,7 +885,8 @@ __global__ __launch_bounds__(256) void attn_kernel(const uint16_t* q, const int3
       le += st_le[k * RT + row];
     }
     const bool empty = !(lr > 0.f);   // a visible key contributes P >= 1 (its max set the reference)
-    const float inv = empty ? 0.f : __builtin_amdgcn_rcpf(lr);   // v_rcp_f32, 1 ulp
+    // v_rcp_f32 (1 ulp); an fp8 cache's scale multiplies the values here
+    const float inv = empty ? 0.f : (KV8 ? a.kv_scale * __builtin_amdgcn_rcpf(lr) : __builtin_amdgcn_rcpf(lr));
     lds_u8* const rowp = sb + row * SPITCH + 256 * w + 8 * g;    // dims 128 w + 4 g of the row
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
@@ -1176,9 +1275,12 @@ int ensure_device() {
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MLA_ERR_HIP;
     const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
     if (ok) {
-      const void* attn[] = {reinterpret_cast<const void*>(attn_kernel<0>),
-                            reinterpret_cast<const void*>(attn_kernel<1>),
-                            reinterpret_cast<const void*>(attn_kernel<2>)};
+      const void* attn[] = {reinterpret_cast<const void*>(attn_kernel<0, false>),
+                            reinterpret_cast<const void*>(attn_kernel<1, false>),
+                            reinterpret_cast<const void*>(attn_kernel<2, false>),
+                            reinterpret_cast<const void*>(attn_kernel<0, true>),
+                            reinterpret_cast<const void*>(attn_kernel<1, true>),
+                            reinterpret_cast<const void*>(attn_kernel<2, true>)};
       bool fail = false;
       for (const void* f : attn)
         fail |= hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kAttnSmemBytes) !=
@@ -1202,7 +1304,7 @@ int launch_status() {
 // Launch the attention kernel.  With partials, part_o / part_lse receive the
 // S split results; otherwise out_lat / lse receive the final result (S == 1).
 int run_attention(const mla_verify_params* p, const mla::Plan& pl, const mla_bf16* q,
-                  const mla_bf16* pool, const int32_t* bt, const int32_t* bounds, mla_bf16* out_lat,
+                  const void* pool, const int32_t* bt, const int32_t* bounds, mla_bf16* out_lat,
                   float* lse, bool partials, mla_bf16* part_o, float* part_lse, hipStream_t stream) {
   AttnArgs a{};
   a.q = q;
@@ -1217,7 +1319,9 @@ int run_attention(const mla_verify_params* p, const mla::Plan& pl, const mla_bf1
   a.N = p->num_pool_pages;
   a.S = pl.splits;
   a.row_tiles = pl.row_tiles;
-  a.scale_log2 = p->sm_scale * kLog2e;
+  // an fp8 cache's scale multiplies every score (and, in the finalize, the values)
+  a.kv_scale = p->kv_dtype == MLA_KV_FP8_E4M3 ? p->kv_scale : 1.0f;
+  a.scale_log2 = p->sm_scale * a.kv_scale * kLog2e;
   a.min_split_pages = pl.min_split_pages;
   a.direct = partials ? 0 : 1;
   if (partials) {
@@ -1231,17 +1335,19 @@ int run_attention(const mla_verify_params* p, const mla::Plan& pl, const mla_bf1
   const unsigned grid =
       (unsigned)((groups + mla::kNumXCDs - 1) / mla::kNumXCDs * mla::kNumXCDs * pl.row_tiles);
   const int mode = pl.shape.mode;
-  if (mode == 0)
-    hipLaunchKernelGGL((attn_kernel<0>), dim3(grid), dim3(256), kAttnSmemBytes, stream, a.q, a.bt, a.bounds,
-                       a.B, a.S, a.row_tiles, a.T, a.H, a.R, a.P, a);
-  else if (mode == 1)
-    hipLaunchKernelGGL((attn_kernel<1>), dim3(grid), dim3(256), kAttnSmemBytes, stream, a.q, a.bt, a.bounds,
-                       a.B, a.S, a.row_tiles, a.T, a.H, a.R, a.P, a);
-  else if (mode == 2)
-    hipLaunchKernelGGL((attn_kernel<2>), dim3(grid), dim3(256), kAttnSmemBytes, stream, a.q, a.bt, a.bounds,
-                       a.B, a.S, a.row_tiles, a.T, a.H, a.R, a.P, a);
+  const bool kv8 = p->kv_dtype == MLA_KV_FP8_E4M3;
+#define MLA_LAUNCH_ATTN(M, F8)                                                                        \
+  hipLaunchKernelGGL((attn_kernel<M, F8>), dim3(grid), dim3(256), kAttnSmemBytes, stream, a.q, a.bt, \
+                     a.bounds, a.B, a.S, a.row_tiles, a.T, a.H, a.R, a.P, a)
+  if (mode == 0 && !kv8) MLA_LAUNCH_ATTN(0, false);
+  else if (mode == 1 && !kv8) MLA_LAUNCH_ATTN(1, false);
+  else if (mode == 2 && !kv8) MLA_LAUNCH_ATTN(2, false);
+  else if (mode == 0) MLA_LAUNCH_ATTN(0, true);
+  else if (mode == 1) MLA_LAUNCH_ATTN(1, true);
+  else if (mode == 2) MLA_LAUNCH_ATTN(2, true);
   else
     return MLA_ERR_SHAPE;
+#undef MLA_LAUNCH_ATTN
   return launch_status();
 }
 
@@ -1255,7 +1361,7 @@ int launch_result() { return launch_status(); }
 extern "C" {
 
 int mla_verify_attn(const mla_verify_params* p, const mla_bf16* q_latent,
-                    const mla_bf16* latent_kv_pages, const int32_t* block_table,
+                    const void* latent_kv_pages, const int32_t* block_table,
                     const int32_t* kv_bounds, mla_bf16* out_latent, float* lse, void* workspace,
                     size_t workspace_bytes, void* stream) {
   int rc = mla::check_params(p);
@@ -1281,7 +1387,7 @@ int mla_verify_attn(const mla_verify_params* p, const mla_bf16* q_latent,
 }
 
 int mla_verify_attn_partials(const mla_verify_params* p, const mla_bf16* q_latent,
-                             const mla_bf16* latent_kv_pages, const int32_t* block_table,
+                             const void* latent_kv_pages, const int32_t* block_table,
                              const int32_t* kv_bounds, mla_bf16* part_o, float* part_lse,
                              void* stream) {
   int rc = mla::check_params(p);
@@ -1310,7 +1416,7 @@ int mla_verify_lse_combine(int num_splits, int rows, const mla_bf16* part_o, con
 }
 
 int mla_verify_attn_gated(const mla_verify_params* p, const mla_bf16* q_latent,
-                          const mla_bf16* latent_kv_pages, const int32_t* block_table,
+                          const void* latent_kv_pages, const int32_t* block_table,
                           const int32_t* kv_bounds, const mla_bf16* w_uv,
                           const mla_bf16* gate_logits, mla_bf16* out, float* lse,
                           mla_bf16* out_latent, void* workspace, size_t workspace_bytes,

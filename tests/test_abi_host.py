@@ -53,7 +53,9 @@ def test_check_accepts_valid(lib):
 @pytest.mark.parametrize("kw,code", [
     (dict(latent_dim=576), -2), (dict(page_size=32), -2), (dict(q_len=0), -2),
     (dict(q_len=17), -2), (dict(num_heads=0), -2), (dict(num_heads=129), -2), (dict(batch=0), -2),
-    (dict(kv_dtype=1), -3), (dict(kv_dtype=7), -3),
+    (dict(kv_dtype=7), -3), (dict(kv_dtype=-1), -3),
+    (dict(kv_dtype=1, kv_scale=0.0), -4), (dict(kv_dtype=1, kv_scale=-0.5), -4),
+    (dict(kv_dtype=1, kv_scale=float("nan")), -4), (dict(kv_dtype=1, kv_scale=float("inf")), -4),
     (dict(sm_scale=0.0), -4), (dict(sm_scale=-1.0), -4), (dict(sm_scale=float("nan")), -4),
     (dict(sm_scale=float("inf")), -4), (dict(num_splits=-1), -4), (dict(num_splits=65), -4),
     (dict(max_pages_per_req=0), -4), (dict(num_pool_pages=0), -4),
@@ -68,10 +70,16 @@ def test_null_params(lib):
     assert lib.mla_verify_workspace_size(ctypes.byref(good()), 0, None) == -1
 
 
-def test_fp8_kv_is_rejected_loudly(lib):
-    p = good(kv_dtype=mv.KV_FP8_E4M3)
-    with pytest.raises(mv.MlaVerifyError, match="MLA_ERR_DTYPE"):
-        mv.verify_workspace_size(p)
+def test_fp8_kv_takes_a_scale(lib):
+    # an fp8 cache plans like a bf16 one; its scale must be finite and positive
+    p = good(kv_dtype=mv.KV_FP8_E4M3, kv_scale=2.0 ** -8)
+    assert mv.verify_check(p) == 0
+    assert mv.verify_workspace_size(p) == mv.verify_workspace_size(good())
+    assert mv.verify_num_splits(p) == mv.verify_num_splits(good())
+    with pytest.raises(mv.MlaVerifyError, match="MLA_ERR_ARG"):
+        mv.verify_workspace_size(good(kv_dtype=mv.KV_FP8_E4M3, kv_scale=0.0))
+    # the bf16 path ignores the field
+    assert mv.verify_check(good(kv_scale=-3.0)) == 0
 
 
 def test_split_plan_and_workspace(lib):

@@ -317,13 +317,13 @@ def test_end_to_end_against_unabsorbed_oracle(cfg):
     assert rel_l2(f64_of(out), r["out"]) < 5e-3
 
 
-def test_fp8_request_raises():
-    log("fp8 KV request is rejected")
+def test_unknown_kv_dtype_raises():
+    log("unknown KV dtype is rejected")
     x = make_config(1)
     d = upload(x, q_latent_bits=oracle_qlat_bits(x))
     with pytest.raises(mv.MlaVerifyError, match="MLA_ERR_DTYPE"):
         mv.verify_attn(d["q_latent"], d["pool"], d["block_table"], d["kv_bounds"], x.sm_scale,
-                       kv_dtype=mv.KV_FP8_E4M3)
+                       kv_dtype=5)
 
 
 # ------------------------------------------------ partials + combine entry points
