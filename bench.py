@@ -71,15 +71,16 @@ def kernel_source_hash() -> str:
 
 def algorithmic(x, gated):
     """Bytes and flops the method must move / do per call (visible keys only):
-    the KV of each request read once, Q, the outputs, the LSEs, the tables;
-    for the gated call also W_UV and the gate."""
+    the KV of each request read once (1 KiB per key in bf16, 512 B in fp8),
+    Q, the outputs, the LSEs, the tables; for the gated call also W_UV and the
+    gate."""
     import numpy as np
     b, t, h = x.shape
     r = t * h
     max_keys = x.block_table.shape[1] * 64
     bounds = np.clip(x.kv_bounds, 0, max_keys)
     n_b = bounds.max(axis=1)
-    kv = int(n_b.sum()) * 512 * 2
+    kv = int(n_b.sum()) * 512 * (1 if getattr(x, "kv_dtype", "bf16") == "fp8" else 2)
     q = b * r * 512 * 2
     lse = b * r * 4
     tables = int(((n_b + 63) // 64).sum()) * 4 + b * t * 4
@@ -107,7 +108,8 @@ def cpu_baseline(x, seconds):
     q_bits = oracle_q_bits(x)
     reps, t0 = 0, time.perf_counter()
     while True:
-        oracle.verify_attention_latent(q_bits, x.pool, x.block_table, x.kv_bounds, x.sm_scale)
+        oracle.verify_attention_latent(q_bits, x.pool, x.block_table, x.kv_bounds, x.sm_scale,
+                                       kv_dtype=x.kv_dtype, kv_scale=x.kv_scale)
         reps += 1
         el = time.perf_counter() - t0
         if el >= seconds or reps >= 50:
@@ -145,7 +147,12 @@ def _per_dispatch(rows, name_part):
     return acc
 
 
-def pmc_report(directory, config):
+def traffic_path(config, kv="bf16"):
+    suffix = "" if kv == "bf16" else f"_{kv}"
+    return os.path.join(ROOT, "profiles", f"traffic_config{config}{suffix}.json")
+
+
+def pmc_report(directory, config, kv="bf16"):
     """Calibrated HBM traffic of the attention kernel from two counter runs."""
     out = {"config": config, "kernel_source_sha": kernel_source_hash()}
     for counter, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
@@ -163,14 +170,14 @@ def pmc_report(directory, config):
                                 "bytes_per_dispatch": round(med * 1024.0 * factor)}
     out["traffic_bytes"] = out["fetch_size"]["bytes_per_dispatch"] + \
         out["write_size"]["bytes_per_dispatch"]
-    path = os.path.join(ROOT, "profiles", f"traffic_config{config}.json")
+    path = traffic_path(config, kv)
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
 
 
-def recorded_traffic(config):
-    path = os.path.join(ROOT, "profiles", f"traffic_config{config}.json")
+def recorded_traffic(config, kv="bf16"):
+    path = traffic_path(config, kv)
     try:
         with open(path) as f:
             rec = json.load(f)
@@ -237,6 +244,8 @@ def main():
     ap.add_argument("--warm", action="store_true", help="one pool copy (cache-warm)")
     ap.add_argument("--noncausal", action="store_true",
                     help="every token of a group sees the group's largest bound (draft-block fold)")
+    ap.add_argument("--kv", choices=["bf16", "fp8"], default="bf16",
+                    help="latent cache storage: bf16, or fp8 E4M3 codes with one scale (2^-8)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
@@ -244,7 +253,7 @@ def main():
     args = ap.parse_args()
 
     if args.pmc_report:
-        pmc_report(args.pmc_report, args.config)
+        pmc_report(args.pmc_report, args.config, args.kv)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -259,7 +268,7 @@ def main():
     import torch
 
     import speculative_verify_attention_absorbed_amd as mv
-    from verify_inputs import make_config
+    from verify_inputs import fp8_cache, make_config
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -273,6 +282,9 @@ def main():
         del src, dst
 
     x = make_config(args.config)
+    fp8 = args.kv == "fp8"
+    if fp8:
+        x = fp8_cache(x)     # the same draws, stored as E4M3 codes
     if args.noncausal:
         x.kv_bounds[:] = x.kv_bounds.max(axis=1, keepdims=True)
     b, t, h = x.shape
@@ -285,11 +297,14 @@ def main():
 
     # ---- device inputs (HBM resident before timing)
     ids = torch.from_numpy(x.pool.page_ids.astype(np.int64)).to(dev)
-    pages = up(x.pool.pages)
+    pages = torch.from_numpy(x.pool.pages).to(dev) if fp8 else up(x.pool.pages)
     n_sets = 1 if args.warm else max(2, min(64, math.ceil(2 * MALL_BYTES / max(alg["kv_bytes"], 1))))
     pools = []
     for _ in range(n_sets):
-        p = torch.full((x.pool.num_pages, 64, 512), float("nan"), dtype=torch.bfloat16, device=dev)
+        if fp8:   # E4M3 codes; unreferenced pages hold the NaN code
+            p = torch.full((x.pool.num_pages, 64, 512), 0x7F, dtype=torch.uint8, device=dev)
+        else:
+            p = torch.full((x.pool.num_pages, 64, 512), float("nan"), dtype=torch.bfloat16, device=dev)
         p[ids] = pages
         pools.append(p)
     bt = torch.from_numpy(x.block_table).to(dev)
@@ -298,7 +313,9 @@ def main():
     w_uv = up(x.w_uv)
     gate = up(x.gate)
     params = mv.VerifyParams.make(b, t, h, x.block_table.shape[1], x.pool.num_pages, x.sm_scale,
-                                  splits, tile_rows=args.tile_rows)
+                                  splits, tile_rows=args.tile_rows,
+                                  kv_dtype=mv.KV_FP8_E4M3 if fp8 else mv.KV_BF16,
+                                  kv_scale=x.kv_scale)
     s_used = mv.verify_num_splits(params, gated)
     tile_used = mv.verify_tile_rows(params, gated)
     ws_bytes = mv.verify_workspace_size(params, gated)
@@ -398,13 +415,14 @@ def main():
     # updates of the same step.  The append writes the group's own latents
     # (gathered beforehand from the positions they already hold, so the pools
     # do not change); the trim works on scratch copies of the lengths and table.
-    kv_us = kv_update_timings(args, x, pools, bt, timed, lib, torch, np)
+    # (the cache updates take bf16 rows; an fp8 cache's writer is not part of this library)
+    kv_us = {} if fp8 else kv_update_timings(args, x, pools, bt, timed, lib, torch, np)
 
     tokens = b * t
     bound = "mfma" if args.config == 5 else "hbm"
     k_gbs = alg["bytes"] / ksec / 1e9
     k_tflops = alg["flops"] / ksec / 1e12
-    traffic = recorded_traffic(args.config)
+    traffic = recorded_traffic(args.config, args.kv)
     if bound == "hbm":
         roof = {"bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
@@ -426,7 +444,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": WORKLOAD_NAMES[args.config], "batch": b, "heads": h, "q_len": t,
+        "config": {"workload": WORKLOAD_NAMES[args.config] + (" fp8-KV" if fp8 else ""),
+                   "batch": b, "heads": h, "q_len": t,
+                   "kv_cache": f"fp8 e4m3, scale {x.kv_scale:g}" if fp8 else "bf16",
                    "num_splits": s_used, "tile_rows": tile_used, "gated": gated,
                    "cache": "warm" if args.warm else f"cold: {n_sets} rotating pool copies",
                    "bounds": "non-causal (group max)" if args.noncausal else "causal per token",
