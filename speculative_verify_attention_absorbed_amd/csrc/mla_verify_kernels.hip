@@ -928,14 +928,78 @@ __global__ __launch_bounds__(256) void attn_kernel(const uint16_t* q, const int3
 }
 
 // LSE merge of the S partials of one row, computed by one wave (lane owns
-// dims 8*lane .. 8*lane+7).  Lane s fetches split s's LSE while every lane
-// fetches its 16 bytes of up to 16 partials in the same round trip; the
-// weights come after.  A partial whose LSE is -inf gets weight 0 through a
-// select, so its (possibly stale) workspace bytes never reach the sum.
-// Returns the row's lse; (-inf, 0) when no split saw a key.
+// dims 8*lane .. 8*lane+7).  Returns the row's lse; (-inf, 0) when no split
+// saw a key.  A partial whose LSE is -inf gets weight 0 through a select, so
+// its (possibly stale) workspace bytes never reach the sum.
+//   S <= 16: every lane loads the S LSEs itself (one address per load across
+//           the wave) next to its 16 bytes of each partial, all in one round
+//           trip, and forms max, weights and sum in its own registers: no
+//           cross-lane reduction on the path.  exp and log run on the
+//           hardware's base-2 units (v_exp_f32, v_log_f32, 1 ulp).
+//   S > 16: lane s fetches split s's LSE, the weights are reduced across
+//           lanes, and the partials stream in batches of 16.
 __device__ __forceinline__ float merge_row(const uint16_t* __restrict__ part_o,
                                            const float* __restrict__ part_lse, int S,
                                            size_t stride_rows, size_t row, int lane, float out[8]) {
+  if (S <= 16) {
+    const int sl = S - 1;
+    float lj[16];
+    uint4 v[16];
+    // split indices clamped to a valid one: the loads are unconditional and
+    // issue back to back; a second batch only when there are more than 8
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const size_t r = (size_t)min(j, sl) * stride_rows + row;
+      lj[j] = part_lse[r];
+      v[j] = ld_stream16(part_o + r * D + lane * 8);
+    }
+    if (S > 8) {
+#pragma unroll
+      for (int j = 8; j < 16; ++j) {
+        const size_t r = (size_t)min(j, sl) * stride_rows + row;
+        lj[j] = part_lse[r];
+        v[j] = ld_stream16(part_o + r * D + lane * 8);
+      }
+    } else {
+#pragma unroll
+      for (int j = 8; j < 16; ++j) {
+        lj[j] = -INFINITY;
+        v[j] = make_uint4(0, 0, 0, 0);
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) mx = j < S ? fmaxf(mx, lj[j]) : mx;
+    if (mx == -INFINITY) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) out[e] = 0.f;
+      return -INFINITY;
+    }
+    float wj[16], total = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      wj[j] = j < S ? __builtin_amdgcn_exp2f((lj[j] - mx) * kLog2e) : 0.f;   // exp(-inf) = 0
+      total += wj[j];
+    }
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (j >= 8 && S <= 8) break;   // uniform
+      const bool use = wj[j] > 0.f;
+      const uint32_t wd[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += use ? wj[j] * bf16_to_f32(wd[e] & 0xFFFFu) : 0.f;
+        acc[2 * e + 1] += use ? wj[j] * bf16_to_f32(wd[e] >> 16) : 0.f;
+      }
+    }
+    const float inv = __builtin_amdgcn_rcpf(total);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = acc[e] * inv;
+    return mx + __builtin_amdgcn_logf(total) * kLn2;
+  }
   constexpr int CH = 16;   // partials in flight per lane
   const float l = (lane < S) ? part_lse[(size_t)lane * stride_rows + row] : -INFINITY;
   uint4 v[CH];
