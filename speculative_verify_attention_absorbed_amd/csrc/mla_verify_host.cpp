@@ -41,13 +41,22 @@ int check_params(const mla_verify_params* p) {
 // 32-row tile.  Up to 64: one 64-row tile stages each page once per split,
 // while two 32-row tiles stage it twice (the second read hits L2) but need
 // half the splits to fill the GPU, so every row has half as many partials to
-// write and merge; the 32-row tiles win while they still leave at least four
-// splits per tile at one workgroup per CU (few, long requests), the 64-row
-// tile otherwise.  More rows: 128-row tiles (each wave owns 32 rows in QK),
-// which keep the number of times a page is re-staged small.
-TileShape choose_shape(int rows, int batch) {
+// write and merge.  A tile's staging and LDS traffic per page do not depend
+// on how many of its rows are real, so the second 32-row tile is worth it
+// only when it is more than half full (more than 48 rows) and the pair still
+// leaves at least four splits per tile at one workgroup per CU (few, long
+// requests); otherwise the 64-row tile.  With a forced split count the
+// tiles are chosen to fill the GPU instead: two 32-row tiles while that still
+// fits one workgroup per CU, else one 64-row tile.  More rows: 128-row tiles
+// (each wave owns 32 rows in QK), which keep the number of times a page is
+// re-staged small.
+TileShape choose_shape(int rows, int batch, int forced_splits) {
   if (rows <= 32) return TileShape{0};
-  if (rows <= 64) return (int64_t)kNumCUs / ((int64_t)batch * 2) >= 4 ? TileShape{0} : TileShape{1};
+  if (rows <= 64) {
+    if (forced_splits > 0)
+      return (int64_t)batch * forced_splits * 2 <= kNumCUs ? TileShape{0} : TileShape{1};
+    return rows > 48 && (int64_t)kNumCUs / ((int64_t)batch * 2) >= 4 ? TileShape{0} : TileShape{1};
+  }
   return TileShape{2};
 }
 
@@ -58,7 +67,8 @@ TileShape shape_for_rows(int tile_rows) {
 Plan make_plan(const mla_verify_params* p, bool gated) {
   Plan pl{};
   pl.rows = p->q_len * p->num_heads;
-  pl.shape = p->tile_rows != 0 ? shape_for_rows(p->tile_rows) : choose_shape(pl.rows, p->batch);
+  pl.shape = p->tile_rows != 0 ? shape_for_rows(p->tile_rows)
+                               : choose_shape(pl.rows, p->batch, p->num_splits);
   pl.row_tiles = (pl.rows + pl.shape.tile_rows() - 1) / pl.shape.tile_rows();
   int s = p->num_splits;
   if (s == 0) {

@@ -34,7 +34,7 @@ struct Plan {
   size_t workspace_bytes;
 };
 
-TileShape choose_shape(int rows, int batch);
+TileShape choose_shape(int rows, int batch, int forced_splits);
 int check_params(const mla_verify_params* p);
 Plan make_plan(const mla_verify_params* p, bool gated);
 bool aligned16(const void* ptr);
