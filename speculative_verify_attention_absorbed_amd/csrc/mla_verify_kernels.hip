@@ -178,6 +178,18 @@ __device__ __forceinline__ void dma_row16(const void* base, uint32_t voff, uint3
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
                ::"v"(voff), "s"(base), "s"(lds) : "memory", "m0");
 }
+// One dword per lane HBM -> LDS: lane l fetches 4 bytes at base + voff and the
+// hardware writes them to LDS byte address lds + 4 l.  Same conventions as
+// dma_row16.
+__device__ __forceinline__ void dma_dword(const void* base, uint32_t voff, uint32_t lds) {
+  const uint64_t bp = reinterpret_cast<uint64_t>(base);
+  const uint64_t bu = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(bp >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)bp);
+  base = reinterpret_cast<const void*>(bu);
+  lds = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               ::"v"(voff), "s"(base), "s"(lds) : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // O^T += V^T P^T for one 16x16 block, written so the accumulator is pinned to
@@ -355,10 +367,28 @@ __global__ __launch_bounds__(256) void attn_kernel(const uint16_t* q, const int3
     dvoff8[j] = (uint32_t)((lane >> 5) * 512 + 16 * ((lane & 31) ^ (k & 15)));
   }
 
+  // ---- the tile's bounds (lane j: token t_lo + j; at most 16 are used) and,
+  // when it fits, the request's whole block-table row (the split's page range
+  // is known only once the bounds are) go to LDS by DMA first, so that their
+  // round trip does not wait behind the Q staging below: memory operations
+  // complete in issue order per wave, and the wait further down lets only
+  // the Q DMAs stay outstanding.  Addresses are clamped into the arrays.
+  const int t_lo = row0 / a.H;
+  const int ntok = (row0 + rows_here - 1) / a.H - t_lo + 1;
+  const bool whole_row = a.P <= mla::kMaxSplitPages;
+  lds_u8* const sm_bnd = sp;   // the P tile is idle until the first unit's softmax
+  if (w == 0)
+    dma_dword(a.bounds, (uint32_t)(b * a.T + min(t_lo + lane, a.T - 1)) * 4u, (uint32_t)(uintptr_t)sm_bnd);
+  if (whole_row) {
+    const int chunks = (a.P + 63) / 64;   // 64 entries per DMA
+    for (int c = w; c < chunks; c += 4)
+      dma_dword(a.bt + (size_t)b * a.P, (uint32_t)min(64 * c + lane, a.P - 1) * 4u,
+                (uint32_t)(uintptr_t)(sm_pid + 64 * c));
+  }
+
   // ---- key-split tiles, where every wave needs every Q row, stage Q^T through
-  // the last unit buffer, issued first: its address needs only the tile, so it
-  // shares the memory round trip of the bounds below and is in LDS by the
-  // time the first unit is issued.
+  // the last unit buffer: its address needs only the tile, and it is in LDS
+  // by the time the first unit lands.
   // (an fp8 unit is smaller than a bf16 Q tile: Q then takes the top of the
   // staging area, and units are issued into it only after Q left)
   const uint32_t qb = KV8 ? (uint32_t)(kBufBytes - RT * 1024) : (uint32_t)(NBUF - 1) * UB;
@@ -370,29 +400,15 @@ __global__ __launch_bounds__(256) void attn_kernel(const uint16_t* q, const int3
       dma_row16(src, dvoff[i & 3], lds0 + qb + (uint32_t)r * 1024u);
     }
   }
-
-  // ---- bounds of the tile's tokens (lane j: token t_lo + j; at most 16) and,
-  // when it fits, the request's whole block-table row (the split's page range
-  // is known only once the bounds are): both loads are issued before either
-  // value is used, so they share one memory round trip.
-  const int t_lo = row0 / a.H;
-  const int ntok = (row0 + rows_here - 1) / a.H - t_lo + 1;
-  const int braw = a.bounds[b * a.T + min(t_lo + lane, a.T - 1)];
-  const bool whole_row = a.P <= mla::kMaxSplitPages;
-  constexpr int kPidPerThread = mla::kMaxSplitPages / kThreads;
-  int pidv[kPidPerThread];   // loaded unconditionally (in-row addresses), used only for a whole row
-#pragma unroll
-  for (int j = 0; j < kPidPerThread; ++j) pidv[j] = a.bt[(size_t)b * a.P + min(tid + kThreads * j, a.P - 1)];
   // the rest of the arguments, fetched together while the bounds are in flight
   asm volatile("" ::"s"(a.pool), "s"(a.out_lat), "s"(a.lse), "s"(a.part_o), "s"(a.part_lse), "s"(a.N),
                "s"(a.scale_log2), "s"(a.direct), "s"(a.min_split_pages)
                : "memory");
+  // bounds and table landed in every wave (only this wave's Q DMAs, issued
+  // after them, may still be outstanding)
+  wait_vm_barrier(KS ? RT / 4 : 0);
+  const int braw = *(const __attribute__((address_space(3))) int32_t*)(sm_bnd + 4 * lane);
   const int tb = (lane < ntok) ? clampi(braw, 0, max_keys) : 0;
-  if (whole_row) {
-#pragma unroll
-    for (int j = 0; j < kPidPerThread; ++j)
-      if (tid + kThreads * j < a.P) sm_pid[tid + kThreads * j] = pidv[j];
-  }
 
   // ---- Q^T of this wave's QK rows: row-split tiles load their own rows
   // straight into registers in the pipeline prologue below, next to unit 0's
@@ -435,10 +451,11 @@ __global__ __launch_bounds__(256) void attn_kernel(const uint16_t* q, const int3
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the Q staging has landed before LDS is released
     return;
   }
-  if (!whole_row)
+  if (!whole_row) {   // a table row past what LDS holds: this split's slice only
     for (int i = tid; i < p_end - p_begin; i += 256) sm_pid[i] = a.bt[b * a.P + p_begin + i];
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  }
   const int pid0 = whole_row ? p_begin : 0;   // sm_pid index of the split's first page
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
   // Stage unit u into buffer u % NBUF.  Key rows past the tile's extent, and
   // rows of a page whose id is out of range, are zero-filled instead (never
