@@ -8,8 +8,10 @@
 // folded row has its own bound kv_bounds[b, r / H].
 //
 // Kernels:
-//   attn_kernel<MODE>    one workgroup (4 waves) per (request, row tile, KV
-//                        split); tiles of 32, 64 or 128 folded rows.  The
+//   attn_kernel<MODE, KV8>  one workgroup (4 waves) per (request, row tile,
+//                        KV split); tiles of 32, 64 or 128 folded rows; a bf16
+//                        or (KV8) an fp8 E4M3 latent cache, whose codes are
+//                        converted exactly to bf16 for the MFMAs.  The
 //                        split's pages stream HBM -> LDS by LDS-DMA
 //                        (XOR-swizzled 16-byte chunks) in 64- or 32-key units,
 //                        the next ones in flight while one is computed.

@@ -193,3 +193,30 @@ def test_fp8_page_permutation_and_repeat_bit_identical():
                               -1).astype(np.int32)
     o2, l2 = check_fp8(x2, upload_fp8(x2, q), q, num_splits=4)
     assert np.array_equal(bits_of(o1), bits_of(o2)) and torch.equal(l1, l2)
+
+
+def test_fp8_long_context_block_table_past_one_split_staging():
+    """fp8 cache with a block-table row longer than one split stages in LDS
+    (1094 page ids for 70000 keys): each split loads its own slice of the row."""
+    log("fp8 long context: B=2 ctx=(70000, 3000) H=8 T=4")
+    x = fp8_cache(build_inputs(batch=2, heads=8, q_len=4, ctx=np.array([70000, 3000]), seed=41,
+                               latent_q=True, q_scale=1536.0))
+    assert x.block_table.shape[1] > 1024
+    d = upload_fp8(x)
+    for s in (0, 3):
+        check_fp8(x, d, x.q_latent, num_splits=s, what=f"fp8 long S{s}")
+
+
+@pytest.mark.parametrize("heads,q_len", [(8, 8), (64, 1)])
+def test_fp8_noncausal_draft_block_equal_bounds(heads, q_len):
+    """fp8 cache, every token of a group sharing one bound (the draft block):
+    lengths on, just before and just after page boundaries, odd lengths that
+    cut a staged key pair, and an empty request."""
+    log(f"fp8 non-causal draft block H={heads} T={q_len}")
+    ctx = np.array([1024, 1023, 1025, 64, 1, 0, 701, 1535])
+    bounds = np.repeat(ctx[:, None], q_len, axis=1).astype(np.int32)
+    x = fp8_cache(build_inputs(batch=len(ctx), heads=heads, q_len=q_len, ctx=ctx, bounds=bounds,
+                               seed=33, latent_q=True, q_scale=1536.0))
+    d = upload_fp8(x)
+    for s in (0, 1, 3):
+        check_fp8(x, d, x.q_latent, num_splits=s, what=f"fp8 equal bounds S{s}")
