@@ -1093,8 +1093,14 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint16_t* __res
 //   W_UV    wave w computes out dims 32 w .. +31 of all 16 rows on MFMA
 //           (A = o_lat tile from LDS, B = W_UV[h] rows straight from memory),
 //           then multiplies by sigmoid(gate).
-template <int RB>
-__global__ __launch_bounds__(kThreads, 3) void gated_epilogue_kernel(
+//   WPRE    (grids that fit one workgroup per CU, i.e. small batches, where
+//           the latency of each step is the cost) W_UV[h] is staged into LDS
+//           by DMA at the start -- each wave its own 32 dims, 1 KiB rows with
+//           16-byte chunks XOR-swizzled by the dim's low bits -- so it lands
+//           while the merge runs, and the MFMA reads it from LDS.
+constexpr int kWuvLdsBytes = DV * D * 2;   // W_UV[h]: 128 dims x 512 bf16
+template <int RB, bool WPRE>
+__global__ __launch_bounds__(kThreads, WPRE ? 1 : 3) void gated_epilogue_kernel(
     const uint16_t* __restrict__ part_o, const float* __restrict__ part_lse,
     const uint16_t* __restrict__ w_uv, const uint16_t* __restrict__ gate,
     uint16_t* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ out_latent,
@@ -1102,11 +1108,23 @@ __global__ __launch_bounds__(kThreads, 3) void gated_epilogue_kernel(
   constexpr int LPR = 64 / RB;   // lanes per row for the LSEs: S <= LPR
   constexpr int CHK = 16 / RB;   // partial loads in flight per row (16 per lane: 3 workgroups fit a CU)
   __shared__ uint4 tile[16 * 64];   // 16 rows x 64 chunks of 16 bytes, chunk c of row r at r*64 + (c ^ (r & 15))
+  extern __shared__ uint4 wuv_lds[];   // WPRE: W_UV[h], dim d's chunk c at d*64 + (c ^ (d & 15))
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, i16 = lane & 15;
   const int h = blockIdx.x % H;
   const int rr0 = (blockIdx.x / H) * 16;
   const size_t rows = (size_t)BT * H;
+  const uint16_t* wh = w_uv + (size_t)h * DV * D;
+  if constexpr (WPRE) {
+    // dims 32 wave .. +31 of W_UV[h]: one 1 KiB row per DMA; lane l fetches
+    // chunk l ^ (d & 15), so chunk c lands at position c ^ (d & 15)
+    const uint32_t base = (uint32_t)(uintptr_t)wuv_lds;
+#pragma unroll 8
+    for (int i = 0; i < 32; ++i) {
+      const int d = 32 * wave + i;
+      dma_row16(wh + (size_t)d * D, 16u * (uint32_t)(lane ^ (d & 15)), base + (uint32_t)d * 1024u);
+    }
+  }
 
   // gate values of this lane's outputs: C[row 4g + i][dim 32 wave + 16 nt + i16]
   float gv[2][4];
@@ -1191,18 +1209,22 @@ __global__ __launch_bounds__(kThreads, 3) void gated_epilogue_kernel(
       }
     }
   }
+  if constexpr (WPRE) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's W_UV rows landed
   __syncthreads();
 
   // ---- out[16 rows][32 dims of this wave] = o_lat[16][512] . W_UV[h][dims][512]^T
   f32x4 acc2[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-  const uint16_t* wh = w_uv + (size_t)h * DV * D;
 #pragma unroll 4
   for (int ks = 0; ks < 16; ++ks) {
     const bf16x8 av = __builtin_bit_cast(bf16x8, tile[i16 * 64 + ((4 * ks + g) ^ i16)]);
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const int d = 32 * wave + 16 * nt + i16;
-      const uint4 bv = *reinterpret_cast<const uint4*>(wh + (size_t)d * D + ks * 32 + 8 * g);
+      uint4 bv;
+      if constexpr (WPRE)
+        bv = wuv_lds[d * 64 + ((4 * ks + g) ^ (d & 15))];
+      else
+        bv = *reinterpret_cast<const uint4*>(wh + (size_t)d * D + ks * 32 + 8 * g);
       acc2[nt] = mfma16(av, __builtin_bit_cast(bf16x8, bv), acc2[nt]);
     }
   }
@@ -1370,6 +1392,11 @@ int ensure_device() {
                 hipSuccess;
       fail |= hipFuncSetAttribute(reinterpret_cast<const void*>(absorb_q_kernel<512>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, DV * 512 * 2) != hipSuccess;
+      const void* epi[] = {reinterpret_cast<const void*>(gated_epilogue_kernel<4, true>),
+                           reinterpret_cast<const void*>(gated_epilogue_kernel<2, true>),
+                           reinterpret_cast<const void*>(gated_epilogue_kernel<1, true>)};
+      for (const void* f : epi)
+        fail |= hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kWuvLdsBytes) != hipSuccess;
       if (fail)
         return MLA_ERR_HIP;
     }
@@ -1525,15 +1552,20 @@ int mla_verify_attn_gated(const mla_verify_params* p, const mla_bf16* q_latent,
   if (rc != MLA_OK) return rc;
   const unsigned grid = (unsigned)(((bt_rows + 15) / 16) * p->num_heads);
   const int S = pl.splits;
-  if (S <= 8)
-    hipLaunchKernelGGL((gated_epilogue_kernel<4>), dim3(grid), dim3(kThreads), 0, st, part_o, part_lse,
-                       w_uv, gate_logits, out, lse, out_latent, bt_rows, p->num_heads, S);
-  else if (S <= 16)
-    hipLaunchKernelGGL((gated_epilogue_kernel<2>), dim3(grid), dim3(kThreads), 0, st, part_o, part_lse,
-                       w_uv, gate_logits, out, lse, out_latent, bt_rows, p->num_heads, S);
-  else
-    hipLaunchKernelGGL((gated_epilogue_kernel<1>), dim3(grid), dim3(kThreads), 0, st, part_o, part_lse,
-                       w_uv, gate_logits, out, lse, out_latent, bt_rows, p->num_heads, S);
+  // a grid that fits one workgroup per CU stages W_UV[h] in LDS up front
+  const bool wpre = grid <= (unsigned)mla::kNumCUs;
+#define MLA_LAUNCH_EPI(RBV, WP)                                                                       \
+  hipLaunchKernelGGL((gated_epilogue_kernel<RBV, WP>), dim3(grid), dim3(kThreads), WP ? kWuvLdsBytes : 0, \
+                     st, part_o, part_lse, w_uv, gate_logits, out, lse, out_latent, bt_rows,            \
+                     p->num_heads, S)
+  if (S <= 8) {
+    if (wpre) MLA_LAUNCH_EPI(4, true); else MLA_LAUNCH_EPI(4, false);
+  } else if (S <= 16) {
+    if (wpre) MLA_LAUNCH_EPI(2, true); else MLA_LAUNCH_EPI(2, false);
+  } else {
+    if (wpre) MLA_LAUNCH_EPI(1, true); else MLA_LAUNCH_EPI(1, false);
+  }
+#undef MLA_LAUNCH_EPI
   return launch_status();
 }
 
