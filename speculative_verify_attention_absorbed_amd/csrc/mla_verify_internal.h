@@ -12,6 +12,7 @@ namespace mla {
 
 constexpr int kNumCUs = 256;           // MI355X compute units
 constexpr int kNumXCDs = 8;            // dies; workgroups are dealt to them round-robin
+constexpr size_t kL2BytesPerXCD = 4u << 20;   // each die's L2
 constexpr int kMaxSplitPages = 1024;   // block-table entries one split stages in LDS
 
 // Shape of one attention workgroup (always four wavefronts).

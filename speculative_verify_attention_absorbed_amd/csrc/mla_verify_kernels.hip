@@ -95,6 +95,7 @@ struct AttnArgs {
   int direct;              // 1: write out_lat/lse, 0: write partials
   int min_split_pages;     // a split holds at least this many pages (m)
   float kv_scale;          // fp8 cache: latent = kv_scale * code value (1 for bf16)
+  int l2_partials;         // partials use plain stores (they stay in the XCD's L2 for the combine)
 };
 
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
@@ -162,6 +163,13 @@ __device__ __forceinline__ void st_stream16(void* p, uint4 v) {
 
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
+// st_stream16 as inline assembly, for a store that sits next to a plain one
+// to the same address in the other arm of a branch: the compiler merges such
+// a pair into one store and drops the nontemporal hint.  The s_nop is the
+// wait state a VALU write of the data registers needs after a 16-byte store.
+__device__ __forceinline__ void st_stream16_asm(void* p, u32x4 v) {
+  asm volatile("global_store_dwordx4 %0, %1, off nt\n\ts_nop 0" ::"v"(p), "v"(v) : "memory");
+}
 // One 1 KiB key row HBM -> LDS without passing through registers: lane l
 // fetches the 16 bytes at base + voff and the hardware writes them to LDS
 // byte address lds + 16 l.  Written as inline assembly so that the compiler,
@@ -256,6 +264,7 @@ __device__ __forceinline__ void wait_vm_barrier(int allowed) {
 // The grid is 8 * ceil(groups / 8) * row_tiles workgroups; returns -1 for the
 // padding ones.
 static_assert((mla::kNumXCDs & (mla::kNumXCDs - 1)) == 0, "XCD count is a power of two");
+__host__ __device__ __forceinline__ bool dealt_layout(int row_tiles) { return row_tiles >= 4; }
 __device__ __forceinline__ int logical_item(int bid, int n_groups, int row_tiles, int rr) {
   const int x = bid % mla::kNumXCDs, pos = bid / mla::kNumXCDs;
   const int per = (n_groups + mla::kNumXCDs - 1) / mla::kNumXCDs;   // group slots per XCD
@@ -337,7 +346,7 @@ __global__ __launch_bounds__(256) void attn_kernel(const uint16_t* q, const int3
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
   const int g = lane >> 4, i16 = lane & 15;
 
-  int id = logical_item(blockIdx.x, a.B * a.S, a.row_tiles, a.row_tiles >= 4);
+  int id = logical_item(blockIdx.x, a.B * a.S, a.row_tiles, dealt_layout(a.row_tiles));
   if (id < 0) return;
   const int rt = id % a.row_tiles;
   id /= a.row_tiles;
@@ -922,7 +931,10 @@ __global__ __launch_bounds__(256) void attn_kernel(const uint16_t* q, const int3
   }
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   // wave w stores tile rows w, w + 4, ...; a split's empty rows are skipped
-  // (the merge never reads a partial whose lse is -inf)
+  // (the merge never reads a partial whose lse is -inf).  Streaming stores,
+  // except for partials that the combine reads back on the same XCD: those
+  // stay in its L2 (they cost a write-back at the kernel's end, and save the
+  // combine's round trip to memory).
   constexpr int RPW = RT / 4;   // rows per wave
   uint16_t* const dst0 = a.direct ? a.out_lat + ((size_t)b * a.R + row0) * D
                                   : a.part_o + ((size_t)s * a.B * a.R + (size_t)b * a.R + row0) * D;
@@ -941,9 +953,15 @@ __global__ __launch_bounds__(256) void attn_kernel(const uint16_t* q, const int3
     const int row = w + 4 * i;
     rowv[i] = *(const lds_u32x4*)(sb + row * SPITCH + 16 * lane);
   }
+  if (a.l2_partials && !a.direct) {
 #pragma unroll
-  for (int i = 0; i < RPW; ++i)
-    if ((live_mask >> i) & 1) st_stream16(dst0 + (size_t)(w + 4 * i) * D + 8 * lane, __builtin_bit_cast(uint4, rowv[i]));
+    for (int i = 0; i < RPW; ++i)
+      if ((live_mask >> i) & 1) *reinterpret_cast<u32x4*>(dst0 + (size_t)(w + 4 * i) * D + 8 * lane) = rowv[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < RPW; ++i)
+      if ((live_mask >> i) & 1) st_stream16_asm(dst0 + (size_t)(w + 4 * i) * D + 8 * lane, rowv[i]);
+  }
 }
 
 // LSE merge of the S partials of one row, computed by one wave (lane owns
@@ -1067,9 +1085,20 @@ __device__ __forceinline__ float merge_row(const uint16_t* __restrict__ part_o,
 __global__ __launch_bounds__(kThreads) void combine_kernel(const uint16_t* __restrict__ part_o,
                                                            const float* __restrict__ part_lse,
                                                            uint16_t* __restrict__ out_lat,
-                                                           float* __restrict__ lse, int rows, int S) {
+                                                           float* __restrict__ lse, int rows, int S,
+                                                           int R, int per) {
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (R > 0) {
+    // after the contiguous attention layout (XCD x ran groups x per .. +per-1,
+    // group = request * S + split): XCD x merges the requests whose first
+    // split it ran, so most partials it reads were written through its L2
+    const int x = blockIdx.x % mla::kNumXCDs;
+    const int b_lo = (x * per + S - 1) / S;
+    const int b_hi = min(rows / R, ((x + 1) * per + S - 1) / S);
+    row = b_lo * R + (blockIdx.x / mla::kNumXCDs) * 4 + (threadIdx.x >> 6);
+    if (row >= b_hi * R) return;
+  }
   if (row >= rows) return;
   float v[8];
   const float l = merge_row(part_o, part_lse, S, (size_t)rows, (size_t)row, lane, v);
@@ -1413,10 +1442,22 @@ int launch_status() {
 
 // Launch the attention kernel.  With partials, part_o / part_lse receive the
 // S split results; otherwise out_lat / lse receive the final result (S == 1).
+// Under the contiguous layout a request's splits run on one XCD.  When the
+// partials fill at most a quarter of each XCD's L2 (the rest holds the pages
+// being streamed), the attention kernel stores them without the streaming
+// hint, so they stay in that L2, and the combine merges each request on the
+// same XCD.
+bool partials_stay_in_l2(const mla_verify_params* p, const mla::Plan& pl) {
+  const size_t part_bytes_per_xcd = (size_t)pl.splits * p->batch * pl.rows * D * 2 / mla::kNumXCDs;
+  return pl.splits > 1 && !dealt_layout(pl.row_tiles) && part_bytes_per_xcd <= mla::kL2BytesPerXCD / 4;
+}
+
 int run_attention(const mla_verify_params* p, const mla::Plan& pl, const mla_bf16* q,
                   const void* pool, const int32_t* bt, const int32_t* bounds, mla_bf16* out_lat,
-                  float* lse, bool partials, mla_bf16* part_o, float* part_lse, hipStream_t stream) {
+                  float* lse, bool partials, mla_bf16* part_o, float* part_lse, hipStream_t stream,
+                  bool l2_partials = false) {
   AttnArgs a{};
+  a.l2_partials = l2_partials ? 1 : 0;
   a.q = q;
   a.pool = pool;
   a.bt = bt;
@@ -1488,11 +1529,25 @@ int mla_verify_attn(const mla_verify_params* p, const mla_bf16* q_latent,
   const int rows = p->batch * pl.rows;
   mla_bf16* part_o = static_cast<mla_bf16*>(workspace);
   float* part_lse = reinterpret_cast<float*>(part_o + (size_t)pl.splits * rows * D);
+  const bool xcd_local = partials_stay_in_l2(p, pl);
   rc = run_attention(p, pl, q_latent, latent_kv_pages, block_table, kv_bounds, out_latent, lse,
-                     pl.use_partials, part_o, part_lse, st);
+                     pl.use_partials, part_o, part_lse, st, xcd_local);
   if (rc != MLA_OK || !pl.use_partials) return rc;
-  hipLaunchKernelGGL(combine_kernel, dim3((rows + 3) / 4), dim3(kThreads), 0, st, part_o, part_lse,
-                     out_latent, lse, rows, pl.splits);
+  if (xcd_local) {
+    // rows grouped by the XCD that ran the request's first split
+    const int per = (p->batch * pl.splits + mla::kNumXCDs - 1) / mla::kNumXCDs;
+    int most = 0;
+    for (int x = 0; x < mla::kNumXCDs; ++x) {
+      const int b_lo = (x * per + pl.splits - 1) / pl.splits;
+      const int b_hi = std::min(p->batch, ((x + 1) * per + pl.splits - 1) / pl.splits);
+      most = std::max(most, (b_hi - b_lo) * pl.rows);
+    }
+    hipLaunchKernelGGL(combine_kernel, dim3(mla::kNumXCDs * ((most + 3) / 4)), dim3(kThreads), 0, st, part_o,
+                       part_lse, out_latent, lse, rows, pl.splits, pl.rows, per);
+  } else {
+    hipLaunchKernelGGL(combine_kernel, dim3((rows + 3) / 4), dim3(kThreads), 0, st, part_o, part_lse,
+                       out_latent, lse, rows, pl.splits, 0, 0);
+  }
   return launch_status();
 }
 
@@ -1509,7 +1564,7 @@ int mla_verify_attn_partials(const mla_verify_params* p, const mla_bf16* q_laten
   rc = ensure_device();
   if (rc != MLA_OK) return rc;
   return run_attention(p, pl, q_latent, latent_kv_pages, block_table, kv_bounds, nullptr, nullptr,
-                       true, part_o, part_lse, static_cast<hipStream_t>(stream));
+                       true, part_o, part_lse, static_cast<hipStream_t>(stream), partials_stay_in_l2(p, pl));
 }
 
 int mla_verify_lse_combine(int num_splits, int rows, const mla_bf16* part_o, const float* part_lse,
@@ -1521,7 +1576,7 @@ int mla_verify_lse_combine(int num_splits, int rows, const mla_bf16* part_o, con
   if (rc != MLA_OK) return rc;
   hipLaunchKernelGGL(combine_kernel, dim3((rows + 3) / 4), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), part_o, part_lse, out_latent, lse, rows,
-                     num_splits);
+                     num_splits, 0, 0);
   return launch_status();
 }
 

@@ -121,6 +121,21 @@ def test_fold_shapes(heads, q_len):
                          what=f"H{heads}T{q_len}S{s}tile{tile}")
 
 
+@pytest.mark.parametrize("batch,splits", [(1, 7), (3, 5), (5, 3), (7, 8), (9, 16), (13, 6)])
+def test_combine_rows_by_xcd_cover_every_request(batch, splits):
+    # the combine after the contiguous layout takes each request on the die
+    # that ran its first split: batch * splits not a multiple of 8 leaves
+    # dies with no request and requests straddling two dies' groups
+    log(f"combine by die: B={batch} S={splits}")
+    rng = np.random.default_rng(batch * 31 + splits)
+    ctx = rng.integers(4, 1200, size=batch)
+    bounds = (ctx[:, None] - 3 + np.arange(4)[None, :]).astype(np.int32)
+    x = build_inputs(batch=batch, heads=8, q_len=4, ctx=ctx, bounds=bounds, seed=batch + splits,
+                     latent_q=True, q_scale=1536.0)
+    d = upload(x)
+    check_latent(x, d, x.q_latent, num_splits=splits, what=f"B{batch}S{splits}")
+
+
 def test_long_context_block_table_past_one_split_staging():
     """A block-table row longer than one split stages in LDS (1024 page ids):
     each split then loads only its own slice of the row.  70000 keys = 1094
