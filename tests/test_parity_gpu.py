@@ -136,6 +136,23 @@ def test_combine_rows_by_xcd_cover_every_request(batch, splits):
     check_latent(x, d, x.q_latent, num_splits=splits, what=f"B{batch}S{splits}")
 
 
+@pytest.mark.parametrize("batch", [13, 40, 64])
+def test_dealt_grid_of_several_rounds(batch):
+    # 128-row tiles, four per request, more workgroups than CUs (the dealt
+    # layout): ties, a request with no visible key and a padded last slot
+    # must still map every (request, split, row tile) exactly once
+    log(f"dealt grid: B={batch} H=64 T=8 S=8")
+    rng = np.random.default_rng(batch)
+    ctx = rng.integers(8, 600, size=batch)
+    ctx[::5] = ctx[0]                      # ties
+    bounds = (ctx[:, None] - 7 + np.arange(8)[None, :]).astype(np.int32)
+    bounds[3] = 0                          # a request with no visible key
+    x = build_inputs(batch=batch, heads=64, q_len=8, ctx=ctx, bounds=bounds, seed=batch,
+                     latent_q=True, q_scale=1536.0)
+    d = upload(x)
+    check_latent(x, d, x.q_latent, num_splits=8, what=f"B{batch}")
+
+
 def test_long_context_block_table_past_one_split_staging():
     """A block-table row longer than one split stages in LDS (1024 page ids):
     each split then loads only its own slice of the row.  70000 keys = 1094
