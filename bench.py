@@ -37,6 +37,7 @@ import csv
 import ctypes
 import glob
 import hashlib
+import re
 import json
 import math
 import os
@@ -52,8 +53,10 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
 MALL_BYTES = 256 << 20
 COPY_PROBE_BYTES = 1 << 30
-KERNEL_SOURCE = os.path.join(ROOT, "speculative_verify_attention_absorbed_amd", "csrc",
-                             "mla_verify_kernels.hip")
+CSRC = os.path.join(ROOT, "speculative_verify_attention_absorbed_amd", "csrc")
+# what decides the kernels that run and their launch shapes
+KERNEL_SOURCES = [os.path.join(CSRC, f) for f in
+                  ("mla_verify_kernels.hip", "mla_verify_host.cpp", "mla_verify_internal.h")]
 
 WORKLOAD_NAMES = {
     1: "tiny verify B=1 H=8 q_len=4 ctx=256 gated",
@@ -65,8 +68,17 @@ WORKLOAD_NAMES = {
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256[:16] of the kernel and launch-planning sources with comments and
+    blank space removed: a stored counter reading stays valid across edits of
+    comments only."""
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()[:16]
 
 
 def algorithmic(x, gated):

@@ -25,10 +25,13 @@
 //                        split), or normalised bf16 partials + fp32 partial
 //                        lse (split-KV).
 //   combine_kernel       LSE merge of the S partials of every row (rows with
-//                        no visible key in any split give (-inf, 0)).
+//                        no visible key in any split give (-inf, 0)); after
+//                        the contiguous layout with small partials, each
+//                        request is merged on the XCD whose L2 holds them.
 //   gated_epilogue_kernel  per (head, 16 rows): LSE merge reading only the
 //                        partials with a nonzero weight, then W_UV (512 -> 128)
-//                        on MFMA and the sigmoid gate; optional o_lat output.
+//                        on MFMA and the sigmoid gate; optional o_lat output;
+//                        small grids stage W_UV[h] in LDS during the merge.
 //   absorb_q_kernel      q_latent = W_UK[h]^T q_nope on bf16 MFMA (fp32
 //                        accumulate, bf16 out), W_UK[h] staged in LDS.
 // The paged-cache updates (KV append, trim) live in mla_kv_update.hip.
