@@ -388,29 +388,41 @@ def main():
             end.record(stream)
             torch.cuda.synchronize()
             return start.elapsed_time(end) / steps, steps, "eager"
-        # capture one rotation cycle (n_sets calls, at least 8) and replay it
+        # capture one rotation cycle (n_sets calls, at least 8) and replay it;
+        # a second graph holds the remainder, so that exactly `steps` calls run
         per_graph = n_sets * max(1, math.ceil(8 / n_sets))
-        g = torch.cuda.CUDAGraph()
-        cap = torch.cuda.Stream()
-        cap.wait_stream(stream)
-        with torch.cuda.stream(cap):
-            with torch.cuda.graph(g, stream=cap):
-                csh = vp(torch.cuda.current_stream().cuda_stream)
-                for i in range(per_graph):
-                    fn(i, csh)
-        stream.wait_stream(cap)
-        torch.cuda.synchronize()
+        n_rep, rem = divmod(steps, per_graph)
+
+        def capture(n):
+            g = torch.cuda.CUDAGraph()
+            cap = torch.cuda.Stream()
+            cap.wait_stream(stream)
+            with torch.cuda.stream(cap):
+                with torch.cuda.graph(g, stream=cap):
+                    csh = vp(torch.cuda.current_stream().cuda_stream)
+                    for i in range(n):
+                        fn(i, csh)
+            stream.wait_stream(cap)
+            torch.cuda.synchronize()
+            return g
+
+        g = capture(per_graph) if n_rep > 0 else None
+        g_rem = capture(rem) if rem > 0 else None
         for _ in range(max(1, warmup // per_graph)):
-            g.replay()
+            if g is not None:
+                g.replay()
+            if g_rem is not None:
+                g_rem.replay()
         torch.cuda.synchronize()
-        n_rep = max(1, round(steps / per_graph))
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         start.record(stream)
         for _ in range(n_rep):
             g.replay()
+        if g_rem is not None:
+            g_rem.replay()
         end.record(stream)
         torch.cuda.synchronize()
-        return (start.elapsed_time(end) / (n_rep * per_graph), n_rep * per_graph,
+        return (start.elapsed_time(end) / steps, steps,
                 f"hipGraph replay ({per_graph} calls per graph)")
 
     # ---- timed region 1: exactly `steps` whole calls
