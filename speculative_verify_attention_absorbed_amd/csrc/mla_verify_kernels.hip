@@ -1443,8 +1443,6 @@ int launch_status() {
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
-// Launch the attention kernel.  With partials, part_o / part_lse receive the
-// S split results; otherwise out_lat / lse receive the final result (S == 1).
 // Under the contiguous layout a request's splits run on one XCD.  When the
 // partials fill at most a quarter of each XCD's L2 (the rest holds the pages
 // being streamed), the attention kernel stores them without the streaming
@@ -1455,6 +1453,9 @@ bool partials_stay_in_l2(const mla_verify_params* p, const mla::Plan& pl) {
   return pl.splits > 1 && !dealt_layout(pl.row_tiles) && part_bytes_per_xcd <= mla::kL2BytesPerXCD / 4;
 }
 
+// Launch the attention kernel.  With partials, part_o / part_lse receive the
+// S split results; otherwise out_lat / lse receive the final result (S == 1).
+// l2_partials: store the partials with plain stores (see partials_stay_in_l2).
 int run_attention(const mla_verify_params* p, const mla::Plan& pl, const mla_bf16* q,
                   const void* pool, const int32_t* bt, const int32_t* bounds, mla_bf16* out_lat,
                   float* lse, bool partials, mla_bf16* part_o, float* part_lse, hipStream_t stream,
