@@ -41,8 +41,9 @@ def draw_case(seed):
     tile = int(rng.choice([0, 0, 32, 64, 128]))
     gated = bool(rng.random() < 0.5)
     kv = "fp8" if rng.random() < 1 / 3 else "bf16"
+    want_latent = bool(rng.random() < 0.5)
     return dict(batch=batch, heads=heads, q_len=q_len, ctx=ctx, bounds=bounds, splits=splits,
-                tile=tile, gated=gated, kv=kv)
+                tile=tile, gated=gated, kv=kv, want_latent=want_latent)
 
 
 def upload_case(x):
@@ -78,15 +79,19 @@ def test_random_shapes_match_oracle(seed):
     if c["gated"]:
         out, lse, lat = mv.verify_attn_gated(d["q_latent"], d["pool"], d["block_table"],
                                              d["kv_bounds"], d["w_uv"], d["gate"], x.sm_scale,
-                                             num_splits=c["splits"], want_latent=True,
-                                             tile_rows=c["tile"], **kv)
+                                             num_splits=c["splits"],
+                                             want_latent=c["want_latent"], tile_rows=c["tile"],
+                                             **kv)
         sync()
         want = oracle.gated_output(o_lat, x.w_uv, x.gate)
         got = f64_of(out)
         assert_lse(lse.cpu().numpy().astype(np.float64), want_lse, f"{what} lse")
         assert_masked_rows_zero(got, want_lse, f"{what} out")
         assert_close_output(got, want, f"{what} gated out")
-        assert_close_output(f64_of(lat), o_lat, f"{what} out_latent")
+        if c["want_latent"]:
+            assert_close_output(f64_of(lat), o_lat, f"{what} out_latent")
+        else:
+            assert lat is None
     else:
         out, lse = mv.verify_attn(d["q_latent"], d["pool"], d["block_table"], d["kv_bounds"],
                                   x.sm_scale, num_splits=c["splits"], tile_rows=c["tile"], **kv)
