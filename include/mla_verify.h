@@ -141,7 +141,12 @@ int mla_verify_tile_rows(const mla_verify_params* p, int gated);
  * Returns MLA_OK or an error code; *bytes is written only on success. */
 int mla_verify_workspace_size(const mla_verify_params* p, int gated, size_t* bytes);
 
-/* Verify attention, latent output.
+/* Verify attention, latent output ("Kimi K3: DSpark speculative decoding
+ * under Helix CP", first commit message, "Per-token primitive": attention
+ * over the paged latent cache with one bound per query token, returning the
+ * per-token LSE, and the (-inf, 0) identity for a token with no visible key;
+ * the group's tokens folded into the head dimension as in the vLLM drafter
+ * page's module docstring).
  *   q_latent        [B, T, H, 512] bf16   absorbed queries (row t*H+h = fold)
  *   latent_kv_pages [N, 64, 512]   bf16   paged latent cache (fp8 E4M3
  *                                         codes, 512 B per key row, when
@@ -164,15 +169,19 @@ int mla_verify_attn(const mla_verify_params* p,
                     void* stream);
 
 /* The attention half of mla_verify_attn on its own: the S = mla_verify_num_splits(p, 0)
- * split-KV results, for a caller that merges them itself (for example after
- * exchanging them between ranks that hold different pages of one request).
+ * split-KV results, for a caller that merges them itself, for example after
+ * exchanging them between ranks that hold different pages of one request
+ * ("Kimi K3: DSpark speculative decoding under Helix CP", "Changes": each
+ * context-parallel rank returns its partial output with its softmax
+ * statistics, and a rank with no visible key returns the (-inf, 0) identity).
  *   part_o    [S, B*T*H, 512] bf16  split s's output, normalised by split s's
  *                                   own softmax sum; rows whose split sees no
  *                                   key are left unwritten
  *   part_lse  [S, B*T*H]      fp32  split s's natural-log LSE (-inf: no key)
- * Partition: the folded rows of a request are processed in tiles of 32, 64
- * or 128 rows (R <= 32, <= 64, larger); a tile sees n = ceil(L / 64) pages,
- * L its largest token bound.  Those pages go to S' = min(S, ceil(n / m))
+ * Partition: the folded rows of a request are processed in tiles of
+ * tr = mla_verify_tile_rows(p, 0) rows (the last tile of a request may be
+ * partial); a tile sees n = ceil(L / 64) pages, L the largest bound among the
+ * tokens of its rows.  Those pages go to S' = min(S, ceil(n / m))
  * contiguous splits, split s < S' holding pages [floor(s n / S'),
  * floor((s+1) n / S')), with m = max(1, floor(ceil(P / S) / 2)); splits
  * s >= S' are empty (lse = -inf).  For a batch of similar lengths S' = S; a

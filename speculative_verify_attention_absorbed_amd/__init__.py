@@ -18,6 +18,7 @@ Entry points (same names as the C ABI, without the ``mla_`` prefix):
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 import os
@@ -43,8 +44,8 @@ LATENT, PAGE, NOPE = 512, 64, 128
 EXPORTED_SYMBOLS = [
     "mla_verify_check", "mla_verify_num_splits", "mla_verify_tile_rows", "mla_verify_workspace_size",
     "mla_verify_attn", "mla_verify_attn_partials", "mla_verify_lse_combine",
-    "mla_verify_attn_gated", "mla_verify_absorb_q", "mla_verify_kv_append", "mla_verify_kv_trim",
-    "mla_verify_status_string",
+    "mla_verify_attn_gated", "mla_verify_absorb_q",
+    "mla_verify_kv_append", "mla_verify_kv_trim", "mla_verify_status_string",
 ]
 
 
@@ -192,6 +193,23 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
+def _alloc_on(stream):
+    """Context in which this module allocates outputs and workspaces: the
+    stream the kernels run on.  torch's caching allocator then returns a
+    freed block to that stream's pool only, so it is not handed to other
+    work while the call's kernels may still use it.  A raw stream handle has
+    no torch stream to allocate on; calls given one must bring their own
+    workspace (checked by the callers)."""
+    torch = _torch()
+    if stream is None or not hasattr(stream, "cuda_stream"):
+        return contextlib.nullcontext()
+    return torch.cuda.stream(stream)
+
+
+def _raw_stream(stream):
+    return stream is not None and not hasattr(stream, "cuda_stream")
+
+
 def _params_from(q_latent, pool, block_table, sm_scale, num_splits, kv_dtype, tile_rows=0,
                  kv_scale=1.0):
     b, t, h, d = q_latent.shape
@@ -208,13 +226,19 @@ def _pool_types(kv_dtype):
     return _bf16_types()
 
 
-def _workspace(params, gated, workspace, device):
+def _workspace(params, gated, workspace, device, stream=None):
+    """The call's workspace: the caller's, or one allocated on the call's
+    stream (a raw stream handle requires the caller's)."""
     torch = _torch()
     need = verify_workspace_size(params, gated)
     if need == 0:
         return None, 0
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+        if _raw_stream(stream):
+            raise ValueError("a raw stream handle needs a caller-owned workspace of "
+                             f"{need} bytes (verify_workspace_size)")
+        with _alloc_on(stream):
+            workspace = torch.empty(need, dtype=torch.uint8, device=device)
     if workspace.device.type != "cuda" or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous GPU tensor")
     nbytes = workspace.numel() * workspace.element_size()
@@ -239,13 +263,14 @@ def verify_attn(q_latent, latent_kv_pages, block_table, kv_bounds, sm_scale, *, 
     _dev_tensor(block_table, "block_table", (b, block_table.shape[1]), (torch.int32,))
     _dev_tensor(kv_bounds, "kv_bounds", (b, t), (torch.int32,))
     dev = q_latent.device
-    if out_latent is None:
-        out_latent = torch.empty((b, t, h, LATENT), dtype=torch.bfloat16, device=dev)
-    if lse is None:
-        lse = torch.empty((b, t, h), dtype=torch.float32, device=dev)
+    with _alloc_on(stream):
+        if out_latent is None:
+            out_latent = torch.empty((b, t, h, LATENT), dtype=torch.bfloat16, device=dev)
+        if lse is None:
+            lse = torch.empty((b, t, h), dtype=torch.float32, device=dev)
     _dev_tensor(out_latent, "out_latent", (b, t, h, LATENT), bf)
     _dev_tensor(lse, "lse", (b, t, h), (torch.float32,))
-    workspace, nbytes = _workspace(params, False, workspace, dev)
+    workspace, nbytes = _workspace(params, False, workspace, dev, stream)
     rc = load_library().mla_verify_attn(
         ctypes.byref(params), _ptr(q_latent), _ptr(latent_kv_pages), _ptr(block_table),
         _ptr(kv_bounds), _ptr(out_latent), _ptr(lse), _ptr(workspace), ctypes.c_size_t(nbytes),
@@ -273,17 +298,18 @@ def verify_attn_gated(q_latent, latent_kv_pages, block_table, kv_bounds, w_uv, g
     _dev_tensor(w_uv, "w_uv", (h, NOPE, LATENT), bf)
     _dev_tensor(gate_logits, "gate_logits", (b, t, h, NOPE), bf)
     dev = q_latent.device
-    if out is None:
-        out = torch.empty((b, t, h, NOPE), dtype=torch.bfloat16, device=dev)
-    if lse is None:
-        lse = torch.empty((b, t, h), dtype=torch.float32, device=dev)
-    if out_latent is None and want_latent:
-        out_latent = torch.empty((b, t, h, LATENT), dtype=torch.bfloat16, device=dev)
+    with _alloc_on(stream):
+        if out is None:
+            out = torch.empty((b, t, h, NOPE), dtype=torch.bfloat16, device=dev)
+        if lse is None:
+            lse = torch.empty((b, t, h), dtype=torch.float32, device=dev)
+        if out_latent is None and want_latent:
+            out_latent = torch.empty((b, t, h, LATENT), dtype=torch.bfloat16, device=dev)
     _dev_tensor(out, "out", (b, t, h, NOPE), bf)
     _dev_tensor(lse, "lse", (b, t, h), (torch.float32,))
     if out_latent is not None:
         _dev_tensor(out_latent, "out_latent", (b, t, h, LATENT), bf)
-    workspace, nbytes = _workspace(params, True, workspace, dev)
+    workspace, nbytes = _workspace(params, True, workspace, dev, stream)
     rc = load_library().mla_verify_attn_gated(
         ctypes.byref(params), _ptr(q_latent), _ptr(latent_kv_pages), _ptr(block_table),
         _ptr(kv_bounds), _ptr(w_uv), _ptr(gate_logits), _ptr(out), _ptr(lse), _ptr(out_latent),
@@ -311,10 +337,11 @@ def verify_attn_partials(q_latent, latent_kv_pages, block_table, kv_bounds, sm_s
     s = verify_num_splits(params)
     rows = b * t * h
     dev = q_latent.device
-    if part_o is None:
-        part_o = torch.empty((s, rows, LATENT), dtype=torch.bfloat16, device=dev)
-    if part_lse is None:
-        part_lse = torch.empty((s, rows), dtype=torch.float32, device=dev)
+    with _alloc_on(stream):
+        if part_o is None:
+            part_o = torch.empty((s, rows, LATENT), dtype=torch.bfloat16, device=dev)
+        if part_lse is None:
+            part_lse = torch.empty((s, rows), dtype=torch.float32, device=dev)
     _dev_tensor(part_o, "part_o", (s, rows, LATENT), bf)
     _dev_tensor(part_lse, "part_lse", (s, rows), (torch.float32,))
     rc = load_library().mla_verify_attn_partials(
@@ -335,10 +362,11 @@ def verify_lse_combine(part_o, part_lse, *, out_latent=None, lse=None, stream=No
     _dev_tensor(part_o, "part_o", (s, rows, LATENT), bf)
     _dev_tensor(part_lse, "part_lse", (s, rows), (torch.float32,))
     dev = part_o.device
-    if out_latent is None:
-        out_latent = torch.empty((rows, LATENT), dtype=torch.bfloat16, device=dev)
-    if lse is None:
-        lse = torch.empty((rows,), dtype=torch.float32, device=dev)
+    with _alloc_on(stream):
+        if out_latent is None:
+            out_latent = torch.empty((rows, LATENT), dtype=torch.bfloat16, device=dev)
+        if lse is None:
+            lse = torch.empty((rows,), dtype=torch.float32, device=dev)
     _dev_tensor(out_latent, "out_latent", (rows, LATENT), bf)
     _dev_tensor(lse, "lse", (rows,), (torch.float32,))
     rc = load_library().mla_verify_lse_combine(int(s), int(rows), _ptr(part_o), _ptr(part_lse),
@@ -355,7 +383,8 @@ def verify_absorb_q(q_nope, w_uk, *, q_latent=None, stream=None):
     _dev_tensor(q_nope, "q_nope", (b, t, h, NOPE), bf)
     _dev_tensor(w_uk, "w_uk", (h, NOPE, LATENT), bf)
     if q_latent is None:
-        q_latent = torch.empty((b, t, h, LATENT), dtype=torch.bfloat16, device=q_nope.device)
+        with _alloc_on(stream):
+            q_latent = torch.empty((b, t, h, LATENT), dtype=torch.bfloat16, device=q_nope.device)
     _dev_tensor(q_latent, "q_latent", (b, t, h, LATENT), bf)
     params = VerifyParams.make(b, t, h, 1, 1, 1.0 / math.sqrt(NOPE))
     rc = load_library().mla_verify_absorb_q(ctypes.byref(params), _ptr(q_nope), _ptr(w_uk),
@@ -399,10 +428,11 @@ def verify_kv_trim(kv_len, accepted, block_table, q_len, *, new_len=None, releas
     _dev_tensor(kv_len, "kv_len", (b,), i32)
     _dev_tensor(accepted, "accepted", (b,), i32)
     _dev_tensor(block_table, "block_table", (b, p), i32)
-    if new_len is None:
-        new_len = torch.empty((b,), dtype=torch.int32, device=kv_len.device)
-    if released_page is None:
-        released_page = torch.empty((b,), dtype=torch.int32, device=kv_len.device)
+    with _alloc_on(stream):
+        if new_len is None:
+            new_len = torch.empty((b,), dtype=torch.int32, device=kv_len.device)
+        if released_page is None:
+            released_page = torch.empty((b,), dtype=torch.int32, device=kv_len.device)
     _dev_tensor(new_len, "new_len", (b,), i32)
     _dev_tensor(released_page, "released_page", (b,), i32)
     rc = load_library().mla_verify_kv_trim(int(b), int(q_len), int(p), _ptr(kv_len), _ptr(accepted),

@@ -6,6 +6,7 @@
 
 #include <cstdint>
 
+#include "mla_launch.h"
 #include "mla_verify.h"
 #include "mla_verify_internal.h"
 
@@ -80,10 +81,9 @@ int mla_verify_kv_append(int batch, int q_len, int max_pages_per_req, int num_po
   rc = mla::device_ready();
   if (rc != MLA_OK) return rc;
   const int tokens = batch * q_len;
-  hipLaunchKernelGGL(kv_append_kernel, dim3((tokens + 3) / 4), dim3(kThreads), 0,
-                     static_cast<hipStream_t>(stream), new_latent, slots, block_table, latent_kv_pages,
-                     bad_slots, tokens, q_len, max_pages_per_req, num_pool_pages);
-  return mla::launch_result();
+  return mla::launch(kv_append_kernel, dim3((tokens + 3) / 4), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
+                     new_latent, slots, block_table, latent_kv_pages, bad_slots, tokens, q_len, max_pages_per_req,
+                     num_pool_pages);
 }
 
 int mla_verify_kv_trim(int batch, int q_len, int max_pages_per_req, const int32_t* kv_len,
@@ -95,10 +95,9 @@ int mla_verify_kv_trim(int batch, int q_len, int max_pages_per_req, const int32_
   if (mla::any_misaligned({kv_len, accepted, new_len, block_table, released_page})) return MLA_ERR_ARG;
   rc = mla::device_ready();
   if (rc != MLA_OK) return rc;
-  hipLaunchKernelGGL(kv_trim_kernel, dim3((batch + kThreads - 1) / kThreads), dim3(kThreads), 0,
-                     static_cast<hipStream_t>(stream), kv_len, accepted, new_len, block_table,
-                     released_page, batch, q_len, max_pages_per_req);
-  return mla::launch_result();
+  return mla::launch(kv_trim_kernel, dim3((batch + kThreads - 1) / kThreads), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), kv_len, accepted, new_len, block_table, released_page, batch,
+                     q_len, max_pages_per_req);
 }
 
 }  // extern "C"

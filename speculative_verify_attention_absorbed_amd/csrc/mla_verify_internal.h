@@ -41,10 +41,9 @@ Plan make_plan(const mla_verify_params* p, bool gated);
 bool aligned16(const void* ptr);
 bool any_null(std::initializer_list<const void*> ptrs);
 bool any_misaligned(std::initializer_list<const void*> ptrs);   // any non-null pointer not 16-byte aligned
-// Device set-up check (gfx950, kernel attributes) and the status of the last
-// launch on this thread; defined with the attention kernels.
+// Device set-up check (gfx950, kernel attributes); defined with the
+// attention kernels.
 int device_ready();
-int launch_result();
 // Sizes of the KV append / trim calls (pure host checks).
 int check_kv_dims(int batch, int q_len, int max_pages_per_req, int num_pool_pages);
 

@@ -42,6 +42,7 @@
 #include <cstdint>
 #include <cstring>
 
+#include "mla_launch.h"
 #include "mla_verify.h"
 #include "mla_verify_internal.h"
 
@@ -1438,11 +1439,6 @@ int ensure_device() {
   return st == 1 ? MLA_OK : MLA_ERR_DEVICE;
 }
 
-int launch_status() {
-  const hipError_t e = hipGetLastError();
-  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
-}
-
 // Under the contiguous layout a request's splits run on one XCD.  When the
 // partials fill at most a quarter of each XCD's L2 (the rest holds the pages
 // being streamed), the attention kernel stores them without the streaming
@@ -1491,26 +1487,20 @@ int run_attention(const mla_verify_params* p, const mla::Plan& pl, const mla_bf1
       (unsigned)((groups + mla::kNumXCDs - 1) / mla::kNumXCDs * mla::kNumXCDs * pl.row_tiles);
   const int mode = pl.shape.mode;
   const bool kv8 = p->kv_dtype == MLA_KV_FP8_E4M3;
-#define MLA_LAUNCH_ATTN(M, F8)                                                                        \
-  hipLaunchKernelGGL((attn_kernel<M, F8>), dim3(grid), dim3(256), kAttnSmemBytes, stream, a.q, a.bt, \
-                     a.bounds, a.B, a.S, a.row_tiles, a.T, a.H, a.R, a.P, a)
-  if (mode == 0 && !kv8) MLA_LAUNCH_ATTN(0, false);
-  else if (mode == 1 && !kv8) MLA_LAUNCH_ATTN(1, false);
-  else if (mode == 2 && !kv8) MLA_LAUNCH_ATTN(2, false);
-  else if (mode == 0) MLA_LAUNCH_ATTN(0, true);
-  else if (mode == 1) MLA_LAUNCH_ATTN(1, true);
-  else if (mode == 2) MLA_LAUNCH_ATTN(2, true);
-  else
-    return MLA_ERR_SHAPE;
-#undef MLA_LAUNCH_ATTN
-  return launch_status();
+  auto go = [&](auto kernel) {
+    return mla::launch(kernel, dim3(grid), dim3(kThreads), kAttnSmemBytes, stream, a.q, a.bt, a.bounds, a.B,
+                       a.S, a.row_tiles, a.T, a.H, a.R, a.P, a);
+  };
+  if (mode == 0) return kv8 ? go(attn_kernel<0, true>) : go(attn_kernel<0, false>);
+  if (mode == 1) return kv8 ? go(attn_kernel<1, true>) : go(attn_kernel<1, false>);
+  if (mode == 2) return kv8 ? go(attn_kernel<2, true>) : go(attn_kernel<2, false>);
+  return MLA_ERR_SHAPE;
 }
 
 }  // namespace
 
 namespace mla {
 int device_ready() { return ensure_device(); }
-int launch_result() { return launch_status(); }
 }  // namespace mla
 
 extern "C" {
@@ -1546,13 +1536,11 @@ int mla_verify_attn(const mla_verify_params* p, const mla_bf16* q_latent,
       const int b_hi = std::min(p->batch, ((x + 1) * per + pl.splits - 1) / pl.splits);
       most = std::max(most, (b_hi - b_lo) * pl.rows);
     }
-    hipLaunchKernelGGL(combine_kernel, dim3(mla::kNumXCDs * ((most + 3) / 4)), dim3(kThreads), 0, st, part_o,
+    return mla::launch(combine_kernel, dim3(mla::kNumXCDs * ((most + 3) / 4)), dim3(kThreads), 0, st, part_o,
                        part_lse, out_latent, lse, rows, pl.splits, pl.rows, per);
-  } else {
-    hipLaunchKernelGGL(combine_kernel, dim3((rows + 3) / 4), dim3(kThreads), 0, st, part_o, part_lse,
-                       out_latent, lse, rows, pl.splits, 0, 0);
   }
-  return launch_status();
+  return mla::launch(combine_kernel, dim3((rows + 3) / 4), dim3(kThreads), 0, st, part_o, part_lse, out_latent,
+                     lse, rows, pl.splits, 0, 0);
 }
 
 int mla_verify_attn_partials(const mla_verify_params* p, const mla_bf16* q_latent,
@@ -1578,11 +1566,59 @@ int mla_verify_lse_combine(int num_splits, int rows, const mla_bf16* part_o, con
   if (mla::any_misaligned({part_o, part_lse, out_latent, lse})) return MLA_ERR_ARG;
   const int rc = ensure_device();
   if (rc != MLA_OK) return rc;
-  hipLaunchKernelGGL(combine_kernel, dim3((rows + 3) / 4), dim3(kThreads), 0,
-                     static_cast<hipStream_t>(stream), part_o, part_lse, out_latent, lse, rows,
-                     num_splits, 0, 0);
-  return launch_status();
+  return mla::launch(combine_kernel, dim3((rows + 3) / 4), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
+                     part_o, part_lse, out_latent, lse, rows, num_splits, 0, 0);
 }
+
+}  // extern "C"
+
+namespace {
+// The gated call after its host checks, with `workspace` holding at least
+// pl.workspace_bytes of device memory.
+int gated_call(const mla_verify_params* p, const mla::Plan& pl, const mla_bf16* q_latent,
+               const void* latent_kv_pages, const int32_t* block_table, const int32_t* kv_bounds,
+               const mla_bf16* w_uv, const mla_bf16* gate_logits, mla_bf16* out, float* lse,
+               mla_bf16* out_latent, void* workspace, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int bt_rows = p->batch * p->q_len;
+  const int rows = bt_rows * p->num_heads;
+  mla_bf16* part_o = static_cast<mla_bf16*>(workspace);
+  float* part_lse = reinterpret_cast<float*>(part_o + (size_t)pl.splits * rows * D);
+  // the partials' store rule is the one mla_verify_attn_partials uses, so the
+  // attention kernel launched on its own is the kernel of this call
+  const int rc = run_attention(p, pl, q_latent, latent_kv_pages, block_table, kv_bounds, nullptr, nullptr, true,
+                     part_o, part_lse, st, partials_stay_in_l2(p, pl));
+  if (rc != MLA_OK) return rc;
+  const unsigned grid = (unsigned)(((bt_rows + 15) / 16) * p->num_heads);
+  const int S = pl.splits;
+  // a grid that fits one workgroup per CU stages W_UV[h] in LDS up front
+  const bool wpre = grid <= (unsigned)mla::kNumCUs;
+  auto go = [&](auto kernel, bool wp) {
+    return mla::launch(kernel, dim3(grid), dim3(kThreads), wp ? kWuvLdsBytes : 0, st, part_o, part_lse, w_uv,
+                       gate_logits, out, lse, out_latent, bt_rows, p->num_heads, S);
+  };
+  if (S <= 8) return wpre ? go(gated_epilogue_kernel<4, true>, true) : go(gated_epilogue_kernel<4, false>, false);
+  if (S <= 16) return wpre ? go(gated_epilogue_kernel<2, true>, true) : go(gated_epilogue_kernel<2, false>, false);
+  return wpre ? go(gated_epilogue_kernel<1, true>, true) : go(gated_epilogue_kernel<1, false>, false);
+}
+
+// Host checks shared by the two gated entry points.
+int gated_checks(const mla_verify_params* p, const mla_bf16* q_latent, const void* latent_kv_pages,
+                 const int32_t* block_table, const int32_t* kv_bounds, const mla_bf16* w_uv,
+                 const mla_bf16* gate_logits, mla_bf16* out, float* lse, mla_bf16* out_latent,
+                 const void* workspace) {
+  const int rc = mla::check_params(p);
+  if (rc != MLA_OK) return rc;
+  if (mla::any_null({q_latent, latent_kv_pages, block_table, kv_bounds, w_uv, gate_logits, out, lse}))
+    return MLA_ERR_NULL;
+  if (mla::any_misaligned({q_latent, latent_kv_pages, block_table, kv_bounds, w_uv, gate_logits, out, lse,
+                           out_latent, workspace}))
+    return MLA_ERR_ARG;
+  return MLA_OK;
+}
+}  // namespace
+
+extern "C" {
 
 int mla_verify_attn_gated(const mla_verify_params* p, const mla_bf16* q_latent,
                           const void* latent_kv_pages, const int32_t* block_table,
@@ -1590,42 +1626,15 @@ int mla_verify_attn_gated(const mla_verify_params* p, const mla_bf16* q_latent,
                           const mla_bf16* gate_logits, mla_bf16* out, float* lse,
                           mla_bf16* out_latent, void* workspace, size_t workspace_bytes,
                           void* stream) {
-  int rc = mla::check_params(p);
+  int rc = gated_checks(p, q_latent, latent_kv_pages, block_table, kv_bounds, w_uv, gate_logits, out, lse,
+                        out_latent, workspace);
   if (rc != MLA_OK) return rc;
-  if (mla::any_null({q_latent, latent_kv_pages, block_table, kv_bounds, w_uv, gate_logits, out, lse}))
-    return MLA_ERR_NULL;
-  if (mla::any_misaligned({q_latent, latent_kv_pages, block_table, kv_bounds, w_uv, gate_logits, out, lse,
-                      out_latent, workspace}))
-    return MLA_ERR_ARG;
   const mla::Plan pl = mla::make_plan(p, true);
   if (workspace == nullptr || workspace_bytes < pl.workspace_bytes) return MLA_ERR_WORKSPACE;
   rc = ensure_device();
   if (rc != MLA_OK) return rc;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const int bt_rows = p->batch * p->q_len;
-  const int rows = bt_rows * p->num_heads;
-  mla_bf16* part_o = static_cast<mla_bf16*>(workspace);
-  float* part_lse = reinterpret_cast<float*>(part_o + (size_t)pl.splits * rows * D);
-  rc = run_attention(p, pl, q_latent, latent_kv_pages, block_table, kv_bounds, nullptr, nullptr, true,
-                     part_o, part_lse, st);
-  if (rc != MLA_OK) return rc;
-  const unsigned grid = (unsigned)(((bt_rows + 15) / 16) * p->num_heads);
-  const int S = pl.splits;
-  // a grid that fits one workgroup per CU stages W_UV[h] in LDS up front
-  const bool wpre = grid <= (unsigned)mla::kNumCUs;
-#define MLA_LAUNCH_EPI(RBV, WP)                                                                       \
-  hipLaunchKernelGGL((gated_epilogue_kernel<RBV, WP>), dim3(grid), dim3(kThreads), WP ? kWuvLdsBytes : 0, \
-                     st, part_o, part_lse, w_uv, gate_logits, out, lse, out_latent, bt_rows,            \
-                     p->num_heads, S)
-  if (S <= 8) {
-    if (wpre) MLA_LAUNCH_EPI(4, true); else MLA_LAUNCH_EPI(4, false);
-  } else if (S <= 16) {
-    if (wpre) MLA_LAUNCH_EPI(2, true); else MLA_LAUNCH_EPI(2, false);
-  } else {
-    if (wpre) MLA_LAUNCH_EPI(1, true); else MLA_LAUNCH_EPI(1, false);
-  }
-#undef MLA_LAUNCH_EPI
-  return launch_status();
+  return gated_call(p, pl, q_latent, latent_kv_pages, block_table, kv_bounds, w_uv, gate_logits, out, lse,
+                    out_latent, workspace, stream);
 }
 
 int mla_verify_absorb_q(const mla_verify_params* p, const mla_bf16* q_nope, const mla_bf16* w_uk,
@@ -1644,12 +1653,10 @@ int mla_verify_absorb_q(const mla_verify_params* p, const mla_bf16* q_nope, cons
   const int items = pairs * (whole ? 1 : 4);
   const unsigned grid = (unsigned)((items + mla::kNumXCDs - 1) / mla::kNumXCDs * mla::kNumXCDs);
   if (whole)
-    hipLaunchKernelGGL(absorb_q_kernel<512>, dim3(grid), dim3(kThreads), DV * 512 * 2,
+    return mla::launch(absorb_q_kernel<512>, dim3(grid), dim3(kThreads), DV * 512 * 2,
                        static_cast<hipStream_t>(stream), q_nope, w_uk, q_latent, bt_rows, p->num_heads);
-  else
-    hipLaunchKernelGGL(absorb_q_kernel<128>, dim3(grid), dim3(kThreads), DV * 128 * 2,
-                       static_cast<hipStream_t>(stream), q_nope, w_uk, q_latent, bt_rows, p->num_heads);
-  return launch_status();
+  return mla::launch(absorb_q_kernel<128>, dim3(grid), dim3(kThreads), DV * 128 * 2,
+                     static_cast<hipStream_t>(stream), q_nope, w_uk, q_latent, bt_rows, p->num_heads);
 }
 
 }  // extern "C"
