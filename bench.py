@@ -1,30 +1,48 @@
 #!/usr/bin/env python3
 """Benchmark: speculative-verify attention (gated NoPE MLA, absorbed) on one MI355X.
 
-A step is one verify call over one batch of synthetic input of the chosen
-workload (default: the TP8-share workload -- 16 requests, 8 heads, k = 7
-draft tokens so q_len 8, 512-d bf16 latent cache, contexts uniform in
-[1024, 1536], 64-token pages scattered in a 4096-page pool).  Inputs are
-resident in HBM when timing starts.  To keep the 256 MB Infinity Cache from
-serving the KV, consecutive calls rotate over enough identical copies of the
-page pool (each at its own address) that the bytes one cycle touches exceed
-twice the cache ("cold"); --warm uses one copy.  Calls are captured into a
-hipGraph and replayed (--eager times plain launches).
+A step is one verify call over one batch of synthetic input.  The headline
+workload (default) is the ragged gated verify batch -- 64 requests, 64 heads,
+k = 7 draft tokens so q_len 8, 512-d bf16 latent cache, contexts log-uniform
+in [128, 8192] with 10 % of tokens at bound 0 and 10 % truncated mid-group,
+64-token pages in a 16384-page pool, 8 KV splits, the fused W_UV + sigmoid
+gate epilogue.  It is the largest single-GPU workload and the one bound by
+the matrix cores.  The four other workloads (tiny gated verify, TP8-share
+verify, split-KV verify, plain decode) are measured in the same run and
+reported under extra.per_config.
 
-Prints one JSON line:
-  value      verify tokens/s of the whole call (every kernel of the call);
-  roofline   the dominant kernel -- the attention kernel, launched on its
-             own through mla_verify_attn_partials (or mla_verify_attn when
-             the call is that single kernel) -- as algorithmic bytes (or
-             flops) per launch over its average duration, measured with HIP
-             events on the stream it is launched on; `traffic` is the HBM
-             traffic rocprofv3 counted for that kernel (FETCH_SIZE +
-             WRITE_SIZE, scaled by the same counters' reading for a copy of
-             known size), reported only while the kernel source is the one
-             that was counted;
-  cpu_baseline  the float64 CPU oracle on a bounded sample of the workload.
+Inputs are resident in HBM when timing starts.  To keep the 256 MB Infinity
+Cache from serving the KV, consecutive calls rotate over enough identical
+copies of the page pool (each at its own address) that one cycle touches
+more than twice the cache ("cold"); --warm uses one copy.  Calls are
+captured into hipGraphs and replayed (--eager times plain launches).
+
+Timing:
+  ms_per_step / value   exactly --steps whole calls between two HIP events
+                        on the stream (after --warmup calls): the mean;
+  timing.*              --samples calls timed one by one (a HIP event pair
+                        around each eagerly launched call, all queued behind
+                        a sleep kernel so the host never starves the GPU):
+                        median, p10, p90;
+  roofline              the dominant kernel (the attention kernel, launched
+                        on its own through mla_verify_attn_partials in the
+                        call's launch configuration, or the whole call when
+                        the call is that one kernel): ITS algorithmic work
+                        (flops, or bytes for an HBM-bound shape: KV, Q,
+                        tables and, when it writes the final output, that
+                        output) over its mean duration from HIP events over
+                        --steps launches; `traffic` is the HBM traffic
+                        rocprofv3 counted for that kernel (FETCH_SIZE +
+                        WRITE_SIZE, scaled by the same counters' reading for
+                        a copy of known size), reported only while the kernel
+                        source is the one that was counted;
+  roofline_call         the whole call's algorithmic work over the call time;
+  cpu_baseline          the unabsorbed float64 CPU oracle (explicit per-head
+                        K/V up-projection) on a length-stratified quarter of
+                        the headline batch, median of --cpu-runs runs.
 
 Other modes:
+  --config N           one workload as the headline (N = 1..5)
   --copy-probe         also launch a 1 GiB device copy (counter calibration)
   --pmc-report DIR     turn rocprofv3 counter CSVs (FETCH_SIZE run in
                        DIR/fetch, WRITE_SIZE run in DIR/write) into the
@@ -37,10 +55,11 @@ import csv
 import ctypes
 import glob
 import hashlib
-import re
 import json
 import math
 import os
+import platform
+import re
 import sys
 import time
 
@@ -51,8 +70,10 @@ if ROOT not in sys.path:
 METRIC = "verify tokens/s + % of binding roofline (HBM GB/s or bf16 MFMA) on 1 MI355X"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
+RIDGE_FLOP_PER_BYTE = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 MALL_BYTES = 256 << 20
 COPY_PROBE_BYTES = 1 << 30
+HEADLINE_CONFIG = 5
 CSRC = os.path.join(ROOT, "speculative_verify_attention_absorbed_amd", "csrc")
 # what decides the kernels that run and their launch shapes
 KERNEL_SOURCES = [os.path.join(CSRC, f) for f in
@@ -81,11 +102,19 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic(x, gated):
-    """Bytes and flops the method must move / do per call (visible keys only):
-    the KV of each request read once (1 KiB per key in bf16, 512 B in fp8),
-    Q, the outputs, the LSEs, the tables; for the gated call also W_UV and the
-    gate."""
+def algorithmic(x, gated, kernel_writes_output):
+    """Bytes and flops the method must move / do per call (visible keys only).
+
+    call:   the KV of each request read once (1 KiB per key in bf16, 512 B in
+            fp8), Q, the outputs, the LSEs, the tables; for the gated call
+            also W_UV and the gate; flops 4*512 per visible (key, row) pair
+            plus the gated epilogue's 2*512*128 per row.
+    kernel: what the attention kernel itself must do: the KV, Q and tables,
+            and the final output + LSE only when it writes them (one split,
+            no epilogue); its flops are the attention's alone.  Split
+            partials and their merge are implementation overheads, counted in
+            neither.
+    """
     import numpy as np
     b, t, h = x.shape
     r = t * h
@@ -102,35 +131,76 @@ def algorithmic(x, gated):
     else:
         out = b * r * 512 * 2
         extra = 0
-    flops = 4 * 512 * int(bounds.sum()) * h
-    if gated:
-        flops += 2 * 512 * 128 * b * r
-    return {"kv_bytes": kv, "bytes": kv + q + lse + tables + out + extra, "flops": flops}
+    attn_flops = 4 * 512 * int(bounds.sum()) * h
+    epi_flops = 2 * 512 * 128 * b * r if gated else 0
+    k_bytes = kv + q + tables + (out + lse if kernel_writes_output else 0)
+    return {"kv_bytes": kv, "bytes": kv + q + lse + tables + out + extra,
+            "flops": attn_flops + epi_flops, "kernel_bytes": k_bytes, "kernel_flops": attn_flops}
 
 
-def cpu_baseline(x, seconds):
-    """Time the float64 oracle (latent definition of the call) on whole batches
-    of the same workload until ~`seconds` of wall time, at least once."""
+def roof(work_bytes, work_flops, seconds):
+    """Achieved rates and the binding roofline for this much work in this time."""
+    gbs = work_bytes / seconds / 1e9
+    tflops = work_flops / seconds / 1e12
+    bound = "mfma" if work_flops / max(work_bytes, 1) >= RIDGE_FLOP_PER_BYTE else "hbm"
+    return {"bound": bound, "gbs": round(gbs, 1), "tflops": round(tflops, 2),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS if bound == "mfma" else gbs / HBM_PEAK_GBS, 4)}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(x, runs):
+    """The unabsorbed float64 oracle (explicit K_h = C W_UK[h]^T, V_h = C
+    W_UV[h]^T per request and head, softmax under each token's bound, gate)
+    on every fourth request of the batch by length, so that the sample keeps
+    the batch's length mix: one warm-up, then the median of `runs` runs,
+    with BLAS threads set to the host cores this process may use."""
+    import numpy as np
     import oracle
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
-    q_bits = oracle_q_bits(x)
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.verify_attention_latent(q_bits, x.pool, x.block_table, x.kv_bounds, x.sm_scale,
-                                       kv_dtype=x.kv_dtype, kv_scale=x.kv_scale)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or reps >= 10000:
-            break
+        from threadpoolctl import threadpool_info, threadpool_limits
+    except ImportError:                      # pragma: no cover
+        threadpool_info = threadpool_limits = None
+    cores = len(os.sched_getaffinity(0))
+    n_keys = np.clip(x.kv_bounds.max(axis=1), 0, None)
+    sample = [int(i) for i in np.argsort(n_keys, kind="stable")[::4]]
     b, t, _ = x.shape
-    return {"value": round(reps * b * t / el, 3), "unit": "verify tokens/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{reps} full batch(es) of the timed workload through the float64 NumPy "
-                      f"oracle (latent definition), {el:.1f} s wall"}
+
+    def once():
+        t0 = time.perf_counter()
+        oracle.verify_attention_mla(x.q_nope, x.w_uk, x.w_uv, x.gate, x.pool, x.block_table,
+                                    x.kv_bounds, x.sm_scale, requests=sample,
+                                    kv_dtype=x.kv_dtype, kv_scale=x.kv_scale)
+        return time.perf_counter() - t0
+
+    threads = 1
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=cores):
+            threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+            once()
+            times = [once() for _ in range(runs)]
+    else:
+        once()
+        times = [once() for _ in range(runs)]
+    med = sorted(times)[len(times) // 2]
+    tokens = len(sample) * t
+    return {"value": round(tokens / med, 3), "unit": "verify tokens/s", "cores": int(threads),
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": f"{len(sample)} of {b} requests (every 4th by length, "
+                      f"{int(n_keys[sample].sum())} of {int(n_keys.sum())} keys), {tokens} verify "
+                      f"tokens through the unabsorbed float64 NumPy oracle; median of {runs} runs "
+                      f"after one warm-up: {med:.2f} s"}
 
 
 def oracle_q_bits(x):
@@ -200,8 +270,117 @@ def recorded_traffic(config, kv="bf16"):
     return rec.get("traffic_bytes")
 
 
-# --------------------------------------------------------------- main
-def kv_update_timings(args, x, pools, bt, timed, lib, torch, np):
+# --------------------------------------------------------------- timing
+class Timer:
+    """Timing of callables fn(i, stream_handle) on the current stream."""
+
+    def __init__(self, torch, eager):
+        self.torch = torch
+        self.eager = eager
+        self.stream = torch.cuda.current_stream()
+        self._cycles_per_ms = None
+
+    def _vp(self, stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+
+    def capture(self, fn, idx):
+        """One graph holding the calls fn(i) for i in idx."""
+        torch = self.torch
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(self.stream)
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                csh = self._vp(torch.cuda.current_stream())
+                for i in idx:
+                    fn(i, csh)
+        self.stream.wait_stream(cap)
+        torch.cuda.synchronize()
+        return g
+
+    def mean_ms(self, fn, steps, warmup, n_sets):
+        """Mean ms per call over exactly `steps` calls between two events."""
+        torch = self.torch
+        sh = self._vp(self.stream)
+        for i in range(max(warmup, 1)):
+            fn(i, sh)
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if self.eager:
+            start.record(self.stream)
+            for i in range(steps):
+                fn(i, sh)
+            end.record(self.stream)
+            torch.cuda.synchronize()
+            return start.elapsed_time(end) / steps, "eager"
+        # capture one rotation cycle (n_sets calls, at least 8) and replay it;
+        # a second graph holds the remainder, so that exactly `steps` calls run
+        per_graph = n_sets * max(1, math.ceil(8 / n_sets))
+        n_rep, rem = divmod(steps, per_graph)
+        g = self.capture(fn, range(per_graph)) if n_rep > 0 else None
+        g_rem = self.capture(fn, range(rem)) if rem > 0 else None
+        for _ in range(max(1, warmup // per_graph)):
+            if g is not None:
+                g.replay()
+            if g_rem is not None:
+                g_rem.replay()
+        torch.cuda.synchronize()
+        start.record(self.stream)
+        for _ in range(n_rep):
+            g.replay()
+        if g_rem is not None:
+            g_rem.replay()
+        end.record(self.stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / steps, f"hipGraph replay ({per_graph} calls per graph)"
+
+    def _sleep_cycles(self, ms):
+        torch = self.torch
+        if self._cycles_per_ms is None:
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(1000)
+            s.record(self.stream)
+            torch.cuda._sleep(1_000_000)
+            e.record(self.stream)
+            torch.cuda.synchronize()
+            self._cycles_per_ms = 1_000_000 / max(s.elapsed_time(e), 1e-3)
+        return int(ms * self._cycles_per_ms)
+
+    def samples(self, fn, n, n_sets):
+        """Durations (ms) of `n` calls timed one by one: an event pair around
+        each call, launched eagerly and all queued behind a sleep kernel so
+        that the GPU runs them back to back (a single-call graph replay per
+        sample would add the graph launch's own gap, about 9 us, to every
+        sample)."""
+        torch = self.torch
+        sh = self._vp(self.stream)
+        for i in range(min(n_sets, n)):
+            fn(i, sh)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        torch.cuda._sleep(self._sleep_cycles(max(5.0, 0.08 * n)))
+        for i in range(n):
+            evs[i][0].record(self.stream)
+            fn(i, sh)
+            evs[i][1].record(self.stream)
+        torch.cuda.synchronize()
+        return sorted(s.elapsed_time(e) for s, e in evs)
+
+
+def stats_us(samples_ms, mean_ms=None):
+    n = len(samples_ms)
+
+    def q(p):
+        return samples_ms[min(n - 1, max(0, int(round(p * (n - 1)))))] * 1e3
+    out = {"median": round(q(0.5), 3), "p10": round(q(0.1), 3), "p90": round(q(0.9), 3), "n": n}
+    if mean_ms is not None:
+        out["mean"] = round(mean_ms * 1e3, 3)
+    return out
+
+
+# --------------------------------------------------------------- one workload
+def kv_update_timings(x, pools, bt, timer, lib, torch, np):
     """Per-call time of mla_verify_kv_append (the B*T group written by slot
     table) and mla_verify_kv_trim, in the same launch mode as the call."""
     dev = bt.device
@@ -234,48 +413,16 @@ def kv_update_timings(args, x, pools, bt, timed, lib, torch, np):
         if rc != 0:
             raise RuntimeError(f"mla_verify_kv_trim: {rc}")
 
-    steps = max(64, args.steps // 4)
-    a_ms, _, _ = timed(append, steps, 8)
-    t_ms, _, _ = timed(trim, steps, 8)
+    a_ms, _ = timer.mean_ms(append, 64, 8, n_sets)
+    t_ms, _ = timer.mean_ms(trim, 64, 8, 1)
     moved = b * t * 2 * 1024
     return {"kv_append_us": round(a_ms * 1e3, 3), "kv_append_bytes": moved,
             "kv_append_gbs": round(moved / (a_ms * 1e-3) / 1e9, 1),
             "kv_trim_us": round(t_ms * 1e3, 3)}
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
-    ap.add_argument("--splits", type=int, default=None, help="force num_splits (0 = library)")
-    ap.add_argument("--tile-rows", type=int, default=0, choices=[0, 32, 64, 128],
-                    help="force rows per attention workgroup (0 = library)")
-    ap.add_argument("--eager", action="store_true", help="time eager launches, not graph replay")
-    ap.add_argument("--warm", action="store_true", help="one pool copy (cache-warm)")
-    ap.add_argument("--noncausal", action="store_true",
-                    help="every token of a group sees the group's largest bound (draft-block fold)")
-    ap.add_argument("--kv", choices=["bf16", "fp8"], default="bf16",
-                    help="latent cache storage: bf16, or fp8 E4M3 codes with one scale (2^-8)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-probe", action="store_true")
-    ap.add_argument("--pmc-report", metavar="DIR")
-    args = ap.parse_args()
-
-    if args.pmc_report:
-        pmc_report(args.pmc_report, args.config, args.kv)
-        return
-
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        if int(os.environ.get("RANK", "0")) == 0:
-            print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
-                  f"{world}); this verify-attention path does not shard across GPUs.",
-                  file=sys.stderr)
-        sys.exit(2)
-
+def measure(cfg, args, steps, warmup, n_samples, lib, timer, with_kv_updates):
+    """Build workload `cfg` in HBM and time its call and its attention kernel."""
     import numpy as np
     import torch
 
@@ -283,17 +430,7 @@ def main():
     from verify_inputs import fp8_cache, make_config
 
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    lib = mv.load_library()
-
-    if args.copy_probe:      # counter calibration: one copy of known size
-        src = torch.empty(COPY_PROBE_BYTES // 2, dtype=torch.int16, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-
-    x = make_config(args.config)
+    x = make_config(cfg, sharp=args.scores == "sharp")
     fp8 = args.kv == "fp8"
     if fp8:
         x = fp8_cache(x)     # the same draws, stored as E4M3 codes
@@ -302,15 +439,15 @@ def main():
     b, t, h = x.shape
     gated = x.gated
     splits = x.num_splits if args.splits is None else args.splits
-    alg = algorithmic(x, gated)
 
     def up(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
     # ---- device inputs (HBM resident before timing)
+    kv_bytes = int(np.clip(x.kv_bounds.max(axis=1), 0, None).sum()) * (512 if fp8 else 1024)
     ids = torch.from_numpy(x.pool.page_ids.astype(np.int64)).to(dev)
     pages = torch.from_numpy(x.pool.pages).to(dev) if fp8 else up(x.pool.pages)
-    n_sets = 1 if args.warm else max(2, min(64, math.ceil(2 * MALL_BYTES / max(alg["kv_bytes"], 1))))
+    n_sets = 1 if args.warm else max(2, min(64, math.ceil(2 * MALL_BYTES / max(kv_bytes, 1))))
     pools = []
     for _ in range(n_sets):
         if fp8:   # E4M3 codes; unreferenced pages hold the NaN code
@@ -319,6 +456,7 @@ def main():
             p = torch.full((x.pool.num_pages, 64, 512), float("nan"), dtype=torch.bfloat16, device=dev)
         p[ids] = pages
         pools.append(p)
+    del pages
     bt = torch.from_numpy(x.block_table).to(dev)
     bounds = torch.from_numpy(x.kv_bounds).to(dev)
     q_lat = mv.verify_absorb_q(up(x.q_nope), up(x.w_uk))     # HIP absorption, outside the timing
@@ -333,10 +471,7 @@ def main():
     ws_bytes = mv.verify_workspace_size(params, gated)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     rows = b * t * h
-    if gated:
-        out = torch.empty((b, t, h, 128), dtype=torch.bfloat16, device=dev)
-    else:
-        out = torch.empty((b, t, h, 512), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((b, t, h, 128 if gated else 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((b, t, h), dtype=torch.float32, device=dev)
     # the attention kernel alone: partials (split or gated calls) or the whole
     # call when it is that single kernel
@@ -372,95 +507,136 @@ def main():
         if rc != 0:
             raise mv.MlaVerifyError(rc, "bench attention kernel")
 
-    def timed(fn, steps, warmup):
-        """Average ms per `fn` call: W warm-up calls, then `steps` calls
-        bracketed by HIP events on the stream they run on."""
-        stream = torch.cuda.current_stream()
-        sh = vp(stream.cuda_stream)
-        for i in range(max(warmup, 1)):
-            fn(i, sh)
-        torch.cuda.synchronize()
-        if args.eager:
-            start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            start.record(stream)
-            for i in range(steps):
-                fn(i, sh)
-            end.record(stream)
-            torch.cuda.synchronize()
-            return start.elapsed_time(end) / steps, steps, "eager"
-        # capture one rotation cycle (n_sets calls, at least 8) and replay it;
-        # a second graph holds the remainder, so that exactly `steps` calls run
-        per_graph = n_sets * max(1, math.ceil(8 / n_sets))
-        n_rep, rem = divmod(steps, per_graph)
-
-        def capture(n):
-            g = torch.cuda.CUDAGraph()
-            cap = torch.cuda.Stream()
-            cap.wait_stream(stream)
-            with torch.cuda.stream(cap):
-                with torch.cuda.graph(g, stream=cap):
-                    csh = vp(torch.cuda.current_stream().cuda_stream)
-                    for i in range(n):
-                        fn(i, csh)
-            stream.wait_stream(cap)
-            torch.cuda.synchronize()
-            return g
-
-        g = capture(per_graph) if n_rep > 0 else None
-        g_rem = capture(rem) if rem > 0 else None
-        for _ in range(max(1, warmup // per_graph)):
-            if g is not None:
-                g.replay()
-            if g_rem is not None:
-                g_rem.replay()
-        torch.cuda.synchronize()
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        start.record(stream)
-        for _ in range(n_rep):
-            g.replay()
-        if g_rem is not None:
-            g_rem.replay()
-        end.record(stream)
-        torch.cuda.synchronize()
-        return (start.elapsed_time(end) / steps, steps,
-                f"hipGraph replay ({per_graph} calls per graph)")
-
-    # ---- timed region 1: exactly `steps` whole calls
-    ms, steps, mode = timed(call, args.steps, args.warmup)
-    sec = ms * 1e-3
-    # ---- timed region 2: the attention kernel alone (same launch configuration)
+    # ---- timed region: exactly `steps` whole calls, then per-call samples
+    ms, mode = timer.mean_ms(call, steps, warmup, n_sets)
+    call_samples = timer.samples(call, n_samples, n_sets)
+    # ---- the attention kernel alone (same launch configuration)
     if attn_alone_is_call:
-        kms = ms
+        kms, k_samples = ms, call_samples
     else:
-        kms, _, _ = timed(attn_only, args.steps, args.warmup)
-    ksec = kms * 1e-3
+        kms, _ = timer.mean_ms(attn_only, steps, warmup, n_sets)
+        k_samples = timer.samples(attn_only, n_samples, n_sets)
+    # the cache updates of the same step (reported, not in the value): the
+    # append writes the group's own latents (gathered beforehand from the
+    # positions they already hold, so the pools do not change); the trim works
+    # on scratch copies of the lengths and table.  They take bf16 rows.
+    kv_us = kv_update_timings(x, pools, bt, timer, lib, torch, np) if (with_kv_updates and not fp8) else {}
 
-    # ---- timed region 3 (reported in "extra", not in the value): the cache
-    # updates of the same step.  The append writes the group's own latents
-    # (gathered beforehand from the positions they already hold, so the pools
-    # do not change); the trim works on scratch copies of the lengths and table.
-    # (the cache updates take bf16 rows; an fp8 cache's writer is not part of this library)
-    kv_us = {} if fp8 else kv_update_timings(args, x, pools, bt, timed, lib, torch, np)
-
+    alg = algorithmic(x, gated, kernel_writes_output=attn_alone_is_call)
+    k_roof = roof(alg["kernel_bytes"], alg["kernel_flops"], kms * 1e-3)
+    c_roof = roof(alg["bytes"], alg["flops"], ms * 1e-3)
     tokens = b * t
-    bound = "mfma" if args.config == 5 else "hbm"
-    k_gbs = alg["bytes"] / ksec / 1e9
-    k_tflops = alg["flops"] / ksec / 1e12
-    traffic = recorded_traffic(args.config, args.kv)
-    if bound == "hbm":
-        roof = {"bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
-    else:
-        roof = {"bound": "mfma", "achieved": round(k_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(k_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": traffic}
+    res = {
+        "workload": WORKLOAD_NAMES[cfg] + (" fp8-KV" if fp8 else ""),
+        "config_index": cfg, "batch": b, "heads": h, "q_len": t, "gated": gated,
+        "kv_cache": f"fp8 e4m3, scale {x.kv_scale:g}" if fp8 else "bf16",
+        "num_splits": s_used, "tile_rows": tile_used,
+        "cache": "warm" if args.warm else f"cold: {n_sets} rotating pool copies",
+        "bounds": "non-causal (group max)" if args.noncausal else "causal per token",
+        "scores": args.scores, "launch": mode,
+        "verify_tokens_per_call": tokens,
+        "verify_tokens_per_s": round(tokens / (ms * 1e-3), 1),
+        "call_us": stats_us(call_samples, ms),
+        "attention_kernel_us": stats_us(k_samples, kms),
+        "algorithmic_bytes": alg["bytes"], "kv_bytes": alg["kv_bytes"], "flops": alg["flops"],
+        "kernel_bytes": alg["kernel_bytes"], "kernel_flops": alg["kernel_flops"],
+        "kernel": {**k_roof, "kv_gbs": round(alg["kv_bytes"] / (kms * 1e-3) / 1e9, 1)},
+        "call": {**c_roof, "kv_gbs": round(alg["kv_bytes"] / (ms * 1e-3) / 1e9, 1)},
+        "traffic": recorded_traffic(cfg, args.kv),
+        **kv_us,
+    }
+    del pools, ws, part_o, part_lse, q_lat
+    return res, x, ms
 
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--samples", type=int, default=200, help="calls timed one by one (median, p10, p90)")
+    ap.add_argument("--config", type=int, default=HEADLINE_CONFIG, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="measure only the headline workload (no extra.per_config)")
+    ap.add_argument("--splits", type=int, default=None, help="force num_splits (0 = library)")
+    ap.add_argument("--tile-rows", type=int, default=0, choices=[0, 32, 64, 128],
+                    help="force rows per attention workgroup (0 = library)")
+    ap.add_argument("--eager", action="store_true", help="time eager launches, not graph replay")
+    ap.add_argument("--warm", action="store_true", help="one pool copy (cache-warm)")
+    ap.add_argument("--noncausal", action="store_true",
+                    help="every token of a group sees the group's largest bound (draft-block fold)")
+    ap.add_argument("--scores", choices=["stated", "sharp"], default="stated",
+                    help="query scale: the stated draws, or the sharp variant (scaled-score spread ~3)")
+    ap.add_argument("--kv", choices=["bf16", "fp8"], default="bf16",
+                    help="latent cache storage: bf16, or fp8 E4M3 codes with one scale (2^-8)")
+    ap.add_argument("--cpu-runs", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--pmc-report", metavar="DIR")
+    args = ap.parse_args()
+
+    if args.pmc_report:
+        pmc_report(args.pmc_report, args.config, args.kv)
+        return
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        if int(os.environ.get("RANK", "0")) == 0:
+            print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
+                  f"{world}); this verify-attention path does not shard across GPUs.",
+                  file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import speculative_verify_attention_absorbed_amd as mv
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = mv.load_library()
+    timer = Timer(torch, args.eager)
+
+    if args.copy_probe:      # counter calibration: one copy of known size
+        src = torch.empty(COPY_PROBE_BYTES // 2, dtype=torch.int16, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    head, x, ms = measure(args.config, args, args.steps, args.warmup, args.samples, lib, timer, True)
+    per_config = {}
+    if not args.no_per_config:
+        for cfg in sorted(WORKLOAD_NAMES):
+            if cfg == args.config:
+                continue
+            r, _, _ = measure(cfg, args, 200, 20, args.samples, lib, timer, False)
+            per_config[str(cfg)] = r
+            torch.cuda.empty_cache()
+
+    k = head["kernel"]
+    c = head["call"]
+    bound = k["bound"]
+    if bound == "hbm":
+        roofline = {"bound": "hbm", "achieved": k["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": k["hbm_frac"], "traffic": head["traffic"]}
+    else:
+        roofline = {"bound": "mfma", "achieved": k["tflops"], "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": k["mfma_frac"], "traffic": head["traffic"]}
+    if c["bound"] == "hbm":
+        roofline_call = {"bound": "hbm", "achieved": c["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": c["hbm_frac"]}
+    else:
+        roofline_call = {"bound": "mfma", "achieved": c["tflops"], "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": c["mfma_frac"]}
+    cfg_out = {k2: head[k2] for k2 in ("workload", "batch", "heads", "q_len", "kv_cache",
+                                       "num_splits", "tile_rows", "gated", "cache", "bounds",
+                                       "scores", "launch")}
     rec = {
         "metric": METRIC,
-        "value": round(tokens / sec, 1),
+        "value": round(head["verify_tokens_per_call"] / (ms * 1e-3), 1),
         "unit": "verify tokens/s",
         "n_gpus": 1,
-        "steps": steps,
+        "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 6),
         "higher_is_better": True,
@@ -468,27 +644,17 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": WORKLOAD_NAMES[args.config] + (" fp8-KV" if fp8 else ""),
-                   "batch": b, "heads": h, "q_len": t,
-                   "kv_cache": f"fp8 e4m3, scale {x.kv_scale:g}" if fp8 else "bf16",
-                   "num_splits": s_used, "tile_rows": tile_used, "gated": gated,
-                   "cache": "warm" if args.warm else f"cold: {n_sets} rotating pool copies",
-                   "bounds": "non-causal (group max)" if args.noncausal else "causal per token",
-                   "launch": mode},
-        "roofline": roof,
-        "extra": {"attention_kernel_us": round(kms * 1e3, 3),
-                  "call_us": round(ms * 1e3, 3),
-                  "algorithmic_bytes": alg["bytes"], "kv_bytes": alg["kv_bytes"],
-                  "flops": alg["flops"],
-                  "call_hbm_gbs": round(alg["bytes"] / sec / 1e9, 1),
-                  "call_hbm_frac": round(alg["bytes"] / sec / 1e9 / HBM_PEAK_GBS, 4),
-                  "kernel_attention_tflops": round(k_tflops, 3),
-                  "kernel_mfma_frac": round(k_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                  "kernel_kv_gbs": round(alg["kv_bytes"] / ksec / 1e9, 1),
-                  "kernel_source_sha": kernel_source_hash(), **kv_us},
+        "config": cfg_out,
+        "roofline": roofline,
+        "roofline_call": roofline_call,
+        "timing": {"call_us": head["call_us"], "attention_kernel_us": head["attention_kernel_us"]},
+        "extra": {k2: v for k2, v in head.items() if k2 not in cfg_out},
     }
+    rec["extra"]["kernel_source_sha"] = kernel_source_hash()
+    if per_config:
+        rec["extra"]["per_config"] = per_config
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
+        rec["cpu_baseline"] = cpu_baseline(x, args.cpu_runs)
     print(json.dumps(rec), flush=True)
 
 
