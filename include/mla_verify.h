@@ -104,6 +104,8 @@ enum mla_verify_kv_dtype {
 #define MLA_VERIFY_MAX_Q_LEN 16
 #define MLA_VERIFY_MAX_HEADS 128
 #define MLA_VERIFY_MAX_SPLITS 64
+/* Device scratch behind mla_verify_attn_gated_noalloc (64 MiB per GPU). */
+#define MLA_VERIFY_STATIC_SCRATCH_BYTES (64u << 20)
 
 typedef struct mla_verify_params {
   int32_t batch;             /* B >= 1 requests                              */
@@ -233,6 +235,29 @@ int mla_verify_attn_gated(const mla_verify_params* p,
                           mla_bf16* out_latent,
                           void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/* mla_verify_attn_gated without a workspace argument, for callers that cannot
+ * allocate device memory (code under hipGraph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The split partials go to a static device
+ * array of MLA_VERIFY_STATIC_SCRATCH_BYTES that the library holds on every GPU
+ * it runs on until the process ends; the call itself allocates nothing.
+ *   Limit: the workspace mla_verify_workspace_size(p, 1) reports must fit the
+ *   scratch, else MLA_ERR_WORKSPACE (host check, before any HIP call).
+ *   Concurrency: every call on one GPU uses that GPU's one scratch, so calls
+ *   that overlap on a GPU (other streams, other threads) race; serialise
+ *   them.  Nothing in the scratch needs clearing between calls.
+ * Other arguments, results and errors as mla_verify_attn_gated. */
+int mla_verify_attn_gated_noalloc(const mla_verify_params* p,
+                                  const mla_bf16* q_latent,
+                                  const void* latent_kv_pages,
+                                  const int32_t* block_table,
+                                  const int32_t* kv_bounds,
+                                  const mla_bf16* w_uv,
+                                  const mla_bf16* gate_logits,
+                                  mla_bf16* out,
+                                  float* lse,
+                                  mla_bf16* out_latent,
+                                  void* stream);
 
 /* Query absorption ("absorbed projections", first page, "What does this PR
  * do?"): q_latent[b,t,h,:] = W_UK[h]^T q_nope[b,t,h,:], fp32 accumulation,

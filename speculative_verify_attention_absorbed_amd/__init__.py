@@ -9,6 +9,8 @@ the library's HIP kernels; there is no fallback path.  If
 Entry points (same names as the C ABI, without the ``mla_`` prefix):
     verify_attn(...)        -> (out_latent [B,T,H,512] bf16, lse [B,T,H] f32)
     verify_attn_gated(...)  -> (out [B,T,H,128] bf16, lse, out_latent or None)
+    verify_attn_gated_noalloc(...) -> the same into caller-given outputs, with the
+                            library's static device scratch instead of a workspace
     verify_absorb_q(...)    -> q_latent [B,T,H,512] bf16
     verify_kv_append(...)   -> None (writes the group's latents into the pool by slot table)
     verify_kv_trim(...)     -> (new_len [B] i32, released_page [B] i32); block_table updated
@@ -26,7 +28,7 @@ import os
 __all__ = [
     "MlaVerifyError", "VerifyParams", "lib_path", "load_library", "verify_check",
     "verify_num_splits", "verify_tile_rows", "verify_workspace_size", "verify_attn",
-    "verify_attn_gated",
+    "verify_attn_gated", "verify_attn_gated_noalloc",
     "verify_absorb_q", "verify_attn_partials", "verify_lse_combine", "verify_kv_append",
     "verify_kv_trim", "status_string",
     "EXPORTED_SYMBOLS",
@@ -44,9 +46,10 @@ LATENT, PAGE, NOPE = 512, 64, 128
 EXPORTED_SYMBOLS = [
     "mla_verify_check", "mla_verify_num_splits", "mla_verify_tile_rows", "mla_verify_workspace_size",
     "mla_verify_attn", "mla_verify_attn_partials", "mla_verify_lse_combine",
-    "mla_verify_attn_gated", "mla_verify_absorb_q",
+    "mla_verify_attn_gated", "mla_verify_attn_gated_noalloc", "mla_verify_absorb_q",
     "mla_verify_kv_append", "mla_verify_kv_trim", "mla_verify_status_string",
 ]
+STATIC_SCRATCH_BYTES = 64 << 20     # MLA_VERIFY_STATIC_SCRATCH_BYTES
 
 
 class MlaVerifyError(RuntimeError):
@@ -105,6 +108,8 @@ def load_library():
     lib.mla_verify_attn.restype = ctypes.c_int
     lib.mla_verify_attn_gated.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.mla_verify_attn_gated.restype = ctypes.c_int
+    lib.mla_verify_attn_gated_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.mla_verify_attn_gated_noalloc.restype = ctypes.c_int
     lib.mla_verify_attn_partials.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
     lib.mla_verify_attn_partials.restype = ctypes.c_int
     lib.mla_verify_lse_combine.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp]
@@ -315,6 +320,37 @@ def verify_attn_gated(q_latent, latent_kv_pages, block_table, kv_bounds, w_uv, g
         _ptr(kv_bounds), _ptr(w_uv), _ptr(gate_logits), _ptr(out), _ptr(lse), _ptr(out_latent),
         _ptr(workspace), ctypes.c_size_t(nbytes), _stream(stream))
     _check(rc, "mla_verify_attn_gated")
+    return out, lse, out_latent
+
+
+def verify_attn_gated_noalloc(q_latent, latent_kv_pages, block_table, kv_bounds, w_uv,
+                              gate_logits, sm_scale, out, lse, *, out_latent=None, num_splits=0,
+                              stream=None, kv_dtype=KV_BF16, tile_rows=0, kv_scale=1.0):
+    """``mla_verify_attn_gated_noalloc``: writes (out, lse, out_latent if given).
+    Every output is the caller's; the library allocates nothing, and its
+    static scratch is shared by all calls on a GPU (overlapping calls race)."""
+    torch = _torch()
+    params = _params_from(q_latent, latent_kv_pages, block_table, sm_scale, num_splits, kv_dtype,
+                          tile_rows, kv_scale)
+    _check(verify_check(params), "mla_verify_attn_gated_noalloc")
+    b, t, h, d = q_latent.shape
+    bf = _bf16_types()
+    _dev_tensor(q_latent, "q_latent", (b, t, h, LATENT), bf)
+    _dev_tensor(latent_kv_pages, "latent_kv_pages", (latent_kv_pages.shape[0], PAGE, LATENT),
+                _pool_types(kv_dtype))
+    _dev_tensor(block_table, "block_table", (b, block_table.shape[1]), (torch.int32,))
+    _dev_tensor(kv_bounds, "kv_bounds", (b, t), (torch.int32,))
+    _dev_tensor(w_uv, "w_uv", (h, NOPE, LATENT), bf)
+    _dev_tensor(gate_logits, "gate_logits", (b, t, h, NOPE), bf)
+    _dev_tensor(out, "out", (b, t, h, NOPE), bf)
+    _dev_tensor(lse, "lse", (b, t, h), (torch.float32,))
+    if out_latent is not None:
+        _dev_tensor(out_latent, "out_latent", (b, t, h, LATENT), bf)
+    rc = load_library().mla_verify_attn_gated_noalloc(
+        ctypes.byref(params), _ptr(q_latent), _ptr(latent_kv_pages), _ptr(block_table),
+        _ptr(kv_bounds), _ptr(w_uv), _ptr(gate_logits), _ptr(out), _ptr(lse), _ptr(out_latent),
+        _stream(stream))
+    _check(rc, "mla_verify_attn_gated_noalloc")
     return out, lse, out_latent
 
 

@@ -1399,9 +1399,20 @@ __global__ __launch_bounds__(kThreads) void absorb_q_kernel(const uint16_t* __re
   }
 }
 
+// Scratch of the allocation-free gated call: the split partials (bf16 O,
+// then fp32 LSE, laid out as the workspace of mla_verify_attn_gated) of one
+// call.  Every GPU the library runs on holds its own copy for the life of the
+// process.  In host code `scratch` names a host-side stand-in, never the
+// device memory: host code uses the per-device address from
+// hipGetSymbolAddress (g_scratch) only.
+}  // namespace
+static __device__ __align__(256) unsigned char scratch[MLA_VERIFY_STATIC_SCRATCH_BYTES];
+namespace {
+
 // ------------------------------------------------------------------ host side
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_device_state[kMaxDevices];   // 0 unknown, 1 gfx950 ready, -1 other
+std::atomic<void*> g_scratch[kMaxDevices];      // device address of `scratch` on each GPU
 
 int ensure_device() {
   int dev = 0;
@@ -1430,8 +1441,12 @@ int ensure_device() {
                            reinterpret_cast<const void*>(gated_epilogue_kernel<1, true>)};
       for (const void* f : epi)
         fail |= hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kWuvLdsBytes) != hipSuccess;
+      // this device's copy of the static scratch (with this device current)
+      void* sp = nullptr;
+      fail |= hipGetSymbolAddress(&sp, HIP_SYMBOL(scratch)) != hipSuccess || sp == nullptr;
       if (fail)
         return MLA_ERR_HIP;
+      g_scratch[dev].store(sp, std::memory_order_release);
     }
     st = ok ? 1 : -1;
     g_device_state[dev].store(st, std::memory_order_release);
@@ -1635,6 +1650,29 @@ int mla_verify_attn_gated(const mla_verify_params* p, const mla_bf16* q_latent,
   if (rc != MLA_OK) return rc;
   return gated_call(p, pl, q_latent, latent_kv_pages, block_table, kv_bounds, w_uv, gate_logits, out, lse,
                     out_latent, workspace, stream);
+}
+
+int mla_verify_attn_gated_noalloc(const mla_verify_params* p, const mla_bf16* q_latent,
+                                  const void* latent_kv_pages, const int32_t* block_table,
+                                  const int32_t* kv_bounds, const mla_bf16* w_uv,
+                                  const mla_bf16* gate_logits, mla_bf16* out, float* lse,
+                                  mla_bf16* out_latent, void* stream) {
+  int rc = gated_checks(p, q_latent, latent_kv_pages, block_table, kv_bounds, w_uv, gate_logits, out, lse,
+                        out_latent, nullptr);
+  if (rc != MLA_OK) return rc;
+  const mla::Plan pl = mla::make_plan(p, true);
+  if (pl.workspace_bytes > (size_t)MLA_VERIFY_STATIC_SCRATCH_BYTES) return MLA_ERR_WORKSPACE;
+  rc = ensure_device();
+  if (rc != MLA_OK) return rc;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+  void* ws = g_scratch[dev].load(std::memory_order_acquire);
+  if (ws == nullptr) return MLA_ERR_HIP;
+  // Nothing in the scratch has to start at zero: the attention kernel writes
+  // every partial LSE of the call (-inf for a split that sees no key of a
+  // row), and the epilogue reads a partial row only when its LSE is finite.
+  return gated_call(p, pl, q_latent, latent_kv_pages, block_table, kv_bounds, w_uv, gate_logits, out, lse,
+                    out_latent, ws, stream);
 }
 
 int mla_verify_absorb_q(const mla_verify_params* p, const mla_bf16* q_nope, const mla_bf16* w_uk,
