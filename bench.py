@@ -240,7 +240,7 @@ def pmc_report(directory, config, kv="bf16"):
     for counter, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
         rows = _counter_rows(os.path.join(directory, sub), counter)
         copy = _per_dispatch(rows, "copy") or _per_dispatch(rows, "elementwise")
-        attn = _per_dispatch(rows, "attn_kernel")
+        attn = _per_dispatch(rows, "attn_")
         if not copy or not attn:
             raise SystemExit(f"{counter}: missing copy probe or attention dispatches in {sub}")
         copy_kib = max(copy.values())          # the 1 GiB probe is the largest copy

@@ -182,12 +182,22 @@ int mla_verify_attn(const mla_verify_params* p,
  *   part_lse  [S, B*T*H]      fp32  split s's natural-log LSE (-inf: no key)
  * Partition: the folded rows of a request are processed in tiles of
  * tr = mla_verify_tile_rows(p, 0) rows (the last tile of a request may be
- * partial); a tile sees n = ceil(L / 64) pages, L the largest bound among the
- * tokens of its rows.  Those pages go to S' = min(S, ceil(n / m))
- * contiguous splits, split s < S' holding pages [floor(s n / S'),
- * floor((s+1) n / S')), with m = max(1, floor(ceil(P / S) / 2)); splits
- * s >= S' are empty (lse = -inf).  For a batch of similar lengths S' = S; a
- * short request in a ragged batch takes fewer splits.
+ * partial); a tile sees the keys below L, the largest bound among the tokens
+ * of its rows.
+ *  - Tiles of 128 rows on a bf16 cache with S >= 2 and B <= 2000 (balanced
+ *    chunks): request b has U_b = ceil(n_b / 32) units of 32 keys, n_b its
+ *    largest bound.  The requests' units laid end to end (request b starting
+ *    at unit st_b = U_0 + ... + U_(b-1), U units in all) are cut into chunks
+ *    of C = max(ceil(U / g), ceil(2 P / (S - 1))) units, g = 8 *
+ *    floor(32 / (tiles per request)); the last chunk runs to the end.  Slot
+ *    j of request b covers the units of chunk floor(st_b / C) + j that
+ *    belong to it, as request keys [32 a, 32 a') (each tile clips them to
+ *    its own L); its slots past its last chunk are empty (lse = -inf).
+ *  - Otherwise a tile's n = ceil(L / 64) pages go to S' = min(S, ceil(n / m))
+ *    contiguous splits, split s < S' holding pages [floor(s n / S'),
+ *    floor((s+1) n / S')), with m = max(1, floor(ceil(P / S) / 2)); splits
+ *    s >= S' are empty (lse = -inf).  For a batch of similar lengths S' = S;
+ *    a short request in a ragged batch takes fewer splits.
  * Combining: lse = ln sum_s exp(lse_s), out = sum_s exp(lse_s - lse) part_o_s
  * (mla_verify_lse_combine).  Errors as mla_verify_attn. */
 int mla_verify_attn_partials(const mla_verify_params* p,

@@ -14,12 +14,15 @@ constexpr int kNumCUs = 256;           // MI355X compute units
 constexpr int kNumXCDs = 8;            // dies; workgroups are dealt to them round-robin
 constexpr size_t kL2BytesPerXCD = 4u << 20;   // each die's L2
 constexpr int kMaxSplitPages = 1024;   // block-table entries one split stages in LDS
+constexpr int kMaxBalancedBatch = 2000;   // requests whose unit prefix sums fit the kernel's LDS
 
 // Shape of one attention workgroup (always four wavefronts).
 //   mode 0: 32-row tile, 64-key staging units, QK split by keys
 //   mode 1: 64-row tile, 64-key staging units, QK split by keys
-//   mode 2: 128-row tile, 32-key staging units, QK split by rows
-// PV always splits the 512 latent dims between the four waves.
+//   mode 2: 128-row tile, 32-key staging units, QK split by rows (fp8 cache)
+// In modes 0-2 PV splits the 512 latent dims between the four waves.
+//   mode 3: 128-row tile, 32-key staging units, bf16 cache: each wave owns
+//           32 rows for QK, softmax and PV alike
 struct TileShape {
   int mode;
   int tile_rows() const { return mode == 0 ? 32 : (mode == 1 ? 64 : 128); }
@@ -32,6 +35,8 @@ struct Plan {
   int splits;           // S
   int min_split_pages;  // m: a request of n pages takes min(S, ceil(n / m)) splits
   bool use_partials;    // results go through the partial workspace (bf16 O, fp32 LSE)
+  bool balanced;        // mode 3 with S >= 2: balanced chunks instead of per-tile splits
+  int chunk_min;        // balanced chunks: minimum chunk in 32-key units, ceil(2 P / (S - 1))
   size_t workspace_bytes;
 };
 

@@ -41,6 +41,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <type_traits>
 
 #include "mla_launch.h"
 #include "mla_verify.h"
@@ -100,6 +101,8 @@ struct AttnArgs {
   int min_split_pages;     // a split holds at least this many pages (m)
   float kv_scale;          // fp8 cache: latent = kv_scale * code value (1 for bf16)
   int l2_partials;         // partials use plain stores (they stay in the XCD's L2 for the combine)
+  int balanced;            // 128-row bf16 tiles: balanced chunks of units per workgroup group
+  int chunk_min;           // balanced chunks: at least this many units per chunk
 };
 
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
@@ -968,6 +971,586 @@ __global__ __launch_bounds__(256) void attn_kernel(const uint16_t* q, const int3
   }
 }
 
+#ifndef MLA_ROWS_AHEAD
+#define MLA_ROWS_AHEAD 3
+#endif
+// Verify attention over one (request b, KV split s, 128-row tile) work item,
+// bf16 cache, with every wave owning 32 folded rows for the whole
+// computation (wave w: tile rows 32 w .. +31):
+//   S^T = K Q^T     bf16 MFMA 16x16x32; K (16 keys x 32 dims) from LDS by
+//                   ds_read_b128, Q^T of the wave's rows in registers; each
+//                   row masked by its own bound.
+//   P               2^(s - ref) in bf16, kept in registers: lane (g, i) of
+//                   the QK output holds keys 4g .. 4g+3 and 16+4g .. 16+4g+3
+//                   of row i, which is the B operand of PV when the PV
+//                   contraction takes the unit's keys in that order.
+//   O^T += V^T P^T  V^T (16 dims x 32 keys in the same key order) from two
+//                   transposing LDS reads; O^T (512 dims x 32 rows) in the
+//                   accumulation registers.
+// No P crosses between waves, so the one barrier per unit is the one that
+// releases a staging buffer.  Softmax as in attn_kernel: each row's reference
+// max is fixed on the split's first unit (a second pass runs past kMaxJump).
+__global__ __launch_bounds__(256) void attn_rows_kernel(const uint16_t* q, const int32_t* bt,
+                                                        const int32_t* bounds, int B, int S, int row_tiles,
+                                                        int T, int H, int R, int P, AttnArgs a) {
+  a.q = q;
+  a.bt = bt;
+  a.bounds = bounds;
+  a.B = B;
+  a.S = S;
+  a.row_tiles = row_tiles;
+  a.T = T;
+  a.H = H;
+  a.R = R;
+  a.P = P;
+  constexpr int RT = 128;                 // rows per tile
+  constexpr int UK = 32;                  // keys per staging unit
+  constexpr int UB = UK * 1024;           // bytes per staging unit
+  constexpr int NBUF = kBufBytes / UB;    // staging units the buffers hold
+  constexpr int ROWS_PW = UK / 4;         // key rows each wave stages per unit
+  constexpr int ND = 32;                  // 16-dim blocks of a row's O
+  constexpr int AHEAD = MLA_ROWS_AHEAD;   // units in flight ahead of the one computed
+  constexpr int KR = 8;                   // K operands in flight (QK)
+  constexpr int VR = 6;                   // V operands in flight (PV)
+  constexpr int SPITCH = 1040;            // staged output row pitch (bytes)
+  static_assert(NBUF == 4 && AHEAD < NBUF, "staging ring");
+  static_assert(RT * SPITCH <= kBufBytes + kPBytes, "row staging");
+
+  extern __shared__ uint4 smem[];
+  lds_u8* sb = (lds_u8*)smem;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)sb;
+  lds_u8* sp = sb + kBufBytes;
+  __attribute__((address_space(3))) int32_t* sm_pid =
+      (__attribute__((address_space(3))) int32_t*)(sb + kBufBytes + kPBytes);
+  lds_f32* sst = (lds_f32*)(sb + kBufBytes + kPBytes + mla::kMaxSplitPages * 4);
+  lds_f32* st_lr = sst;                   // [RT] row sums, for the store mask
+  __attribute__((address_space(3))) int32_t* sm_redo =
+      (__attribute__((address_space(3))) int32_t*)(sst + kStatFloats);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, i16 = lane & 15;
+
+  const int max_keys = a.P * PG;
+
+  // One work item: the rows of row tile rt of request b over a range of its
+  // keys, results into partial slot `slot` (or the outputs, direct mode).
+  // legacy: the range is split `slot` of the tile's own split partition;
+  // otherwise units [ua, ub) (32 keys each) of the request.
+  auto run_item = [&](int b, int rt, int slot, int ua, int ub, bool legacy) {
+  const int s = slot;
+  const int row0 = rt * RT;
+  const int rows_here = min(RT, a.R - row0);
+  __syncthreads();   // LDS of the previous item (staged rows, bounds) is free
+  // lane-dependent address arithmetic is redone per item: made opaque here,
+  // the compiler cannot hoist it out of the item loop, where it would stay
+  // live (and spill) through the key loop
+  int lane_o = threadIdx.x & 63, tid_o = threadIdx.x;
+  asm volatile("" : "+v"(lane_o), "+v"(tid_o));
+  const int lane = lane_o, tid = tid_o, g = lane >> 4, i16 = lane & 15;
+  auto wrow = [&](int rb) { return 32 * w + 16 * rb + i16; };   // tile row of row block rb
+  uint32_t dvoff[4];   // DMA lane offsets of key rows w + 4 j (chunk order swizzled by the row)
+#pragma unroll
+  for (int j = 0; j < 4; ++j) dvoff[j] = 16u * (uint32_t)(lane ^ swz16((w + 4 * j) & 15));
+
+  // ---- the tile's bounds and the request's block-table row to LDS
+  const int t_lo = row0 / a.H;
+  const int ntok = (row0 + rows_here - 1) / a.H - t_lo + 1;
+  const bool whole_row = a.P <= mla::kMaxSplitPages;
+  lds_u8* const sm_bnd = sp;
+  if (w == 0)
+    dma_dword(a.bounds, (uint32_t)(b * a.T + min(t_lo + lane, a.T - 1)) * 4u, (uint32_t)(uintptr_t)sm_bnd);
+  if (whole_row) {
+    const int chunks = (a.P + 63) / 64;
+    for (int c = w; c < chunks; c += 4)
+      dma_dword(a.bt + (size_t)b * a.P, (uint32_t)min(64 * c + lane, a.P - 1) * 4u,
+                (uint32_t)(uintptr_t)(sm_pid + 64 * c));
+  }
+  asm volatile("" ::"s"(a.pool), "s"(a.out_lat), "s"(a.lse), "s"(a.part_o), "s"(a.part_lse), "s"(a.N),
+               "s"(a.scale_log2), "s"(a.direct), "s"(a.min_split_pages)
+               : "memory");
+  wait_vm_barrier(0);
+  const int braw = *(const __attribute__((address_space(3))) int32_t*)(sm_bnd + 4 * lane);
+  const int tb = (lane < ntok) ? clampi(braw, 0, max_keys) : 0;
+
+  int n_tile = tb;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) n_tile = max(n_tile, __shfl_xor(n_tile, off));
+  n_tile = __builtin_amdgcn_readfirstlane(n_tile);
+  int L[2];
+  int lmin = INT_MAX;   // smallest bound among the wave's valid rows
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int r = row0 + wrow(rb);
+    const int lr = __shfl(tb, min(r, a.R - 1) / a.H - t_lo);
+    L[rb] = r < a.R ? lr : 0;
+    if (r < a.R) lmin = min(lmin, lr);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) lmin = min(lmin, __shfl_xor(lmin, off));
+  lmin = __builtin_amdgcn_readfirstlane(lmin);
+  if (lmin == INT_MAX) lmin = 0;   // a wave of padding rows masks every key
+
+  int k_begin, k_end;
+  if (legacy) {
+    const int n_pg = (n_tile + PG - 1) / PG;
+    const int s_eff = min(a.S, max(1, (n_pg + a.min_split_pages - 1) / a.min_split_pages));
+    const int p_begin = s < s_eff ? (s * n_pg) / s_eff : n_pg;
+    const int p_end = s < s_eff ? ((s + 1) * n_pg) / s_eff : n_pg;
+    k_begin = p_begin * PG;
+    k_end = min(p_end * PG, n_tile);
+  } else {
+    k_begin = ua * UK;
+    k_end = min(ub * UK, n_tile);
+  }
+  const int n_units = k_end > k_begin ? (k_end - k_begin + UK - 1) / UK : 0;
+  const int p_first = k_begin / PG;   // first page of the range
+
+  if (n_units == 0 && !a.direct) {
+    for (int r = tid; r < rows_here; r += kThreads)
+      a.part_lse[(size_t)s * a.B * a.R + (size_t)b * a.R + row0 + r] = -INFINITY;
+    return;
+  }
+  if (!whole_row) {   // a table row past what LDS holds: this range's pages only
+    const int n_pages = (k_end - 1) / PG - p_first + 1;
+    for (int i = tid; i < n_pages; i += 256) sm_pid[i] = a.bt[(size_t)b * a.P + p_first + i];
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  }
+  const int pid_base = whole_row ? 0 : p_first;   // sm_pid index of page 0
+
+  // Staging of unit u (32 keys: half a page) into buffer u % NBUF, one key
+  // row per DMA instruction; wave w stages rows w + 4 i.  Rows past the
+  // tile's extent and every row of an out-of-range page id are zero-filled
+  // instead (never read from the pool).
+  struct Stage {
+    const uint16_t* base;   // the unit's first key row in the pool
+    uint32_t buf;           // LDS byte offset of the unit's buffer
+    int valid;              // rows of the unit to fetch
+  };
+  auto stage_of = [&](int u) {
+    Stage st;
+    const int key0 = k_begin + u * UK;   // the unit's first key (a multiple of 32)
+    const int pid = __builtin_amdgcn_readfirstlane(sm_pid[key0 / PG - pid_base]);
+    const bool pid_ok = (unsigned)pid < (unsigned)a.N;
+    st.valid = pid_ok ? n_tile - key0 : 0;
+    st.base = reinterpret_cast<const uint16_t*>(a.pool) + ((size_t)(pid_ok ? pid : 0) * PG + (key0 & 63)) * D;
+    st.buf = (uint32_t)(u % NBUF) * UB;
+    return st;
+  };
+  auto stage_row = [&](const Stage& st, int i, bool full) {   // key row w + 4 i of the unit
+    const int kap = w + 4 * i;
+    if (full || kap < st.valid)
+      dma_row16(st.base + kap * D, dvoff[i & 3], lds0 + st.buf + (uint32_t)kap * 1024u);
+    else
+      *(lds_u32x4*)(sb + st.buf + kap * 1024 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
+  };
+  auto stage_ops = [&](const Stage& st) {   // DMA instructions this wave issues for the unit
+    int ops = 0;
+#pragma unroll
+    for (int i = 0; i < ROWS_PW; ++i) ops += (w + 4 * i) < st.valid;
+    return ops;
+  };
+
+  // K operand: key 16 kb + i16, chunk 4 ks + g  ->  qkb[ks & 3] + 256 (ks >> 2) + 16384 kb
+  const int swl = swz16(i16);
+  uint32_t qkb[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    qkb[j] = (uint32_t)(i16 * 1024 + 64 * (j ^ (swl >> 2)) + 16 * (g ^ (swl & 3)));
+  // V^T operand of dim block d: lanes 4q .. 4q+3 of lane group g address
+  // key 4g + q (first read) and 16 + 4g + q (second), dims 16 d + 4 (i16 & 3)
+  const int vkey = 4 * g + (i16 >> 2);
+  const int vsw = swz16(vkey);
+  const uint32_t vrow = (uint32_t)(vkey * 1024 + 16 * (((i16 & 3) >> 1) ^ (vsw & 1)) + 8 * (i16 & 1));
+  const int vtsw = vsw >> 1;
+
+  bf16x8 qreg[2][16];   // Q[row wrow(rb)][32 ks + 8 g .. +7]
+  f32x4 o[ND][2];       // o[d][rb][i] = O[row wrow(rb)][dim 16 d + 4 g + i]
+  float mref[2], mtrue[2], lround[2], lexact[2], mpreset[2];
+  bool jumped = false;
+  mpreset[0] = mpreset[1] = -INFINITY;
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2v;
+  const bf16x2v ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  // S^T = K Q^T of unit u for the keys 16 kb .. 16 kb + 15:
+  // s[rb][i] = score(key 16 kb + 4 g + i, row wrow(rb)).  after(ks) runs
+  // after the MFMAs of k-step ks (VALU work that overlaps them).
+  auto qk_half = [&](int u, int kb, f32x4 (&s)[2], auto&& after) {
+    const uint32_t kbase = (uint32_t)(u % NBUF) * UB + 16384u * (uint32_t)kb;
+    // even and odd k-steps accumulate apart: four independent MFMA chains,
+    // so no MFMA waits for the result of the one before it
+    f32x4 acc[2][2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) acc[rb][0] = acc[rb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 kop[KR];
+    auto load_k = [&](int ks) { return *(const lds_bf16x8*)(sb + kbase + qkb[ks & 3] + 256 * (ks >> 2)); };
+#pragma unroll
+    for (int ks = 0; ks < KR - 1; ++ks) kop[ks] = load_k(ks);
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) {
+      if (ks + KR - 1 < 16) kop[(ks + KR - 1) % KR] = load_k(ks + KR - 1);
+      mfma16_vacc(acc[0][ks & 1], kop[ks % KR], qreg[0][ks]);
+      mfma16_vacc(acc[1][ks & 1], kop[ks % KR], qreg[1][ks]);
+      after(ks);
+    }
+    // MFMA result -> VALU read: at least 11 wait states after the last MFMA
+    asm volatile("s_nop 7\n\ts_nop 4" : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[1][0]), "+v"(acc[1][1]));
+    s[0] = acc[0][0] + acc[0][1];
+    s[1] = acc[1][0] + acc[1][1];
+  };
+
+  // Raw scores of a key half with the keys a row does not see at -inf (a
+  // unit every valid row of the wave sees in full skips the masking).
+  auto masked = [&](int u, int kb, const f32x4 (&s)[2], float (&sv)[2][4]) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sv[rb][i] = s[rb][i];
+    const int ukey0 = k_begin + u * UK;
+    if (!(ukey0 + UK <= lmin)) {
+      const int key = ukey0 + 16 * kb + 4 * g;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[rb][i] = (key + i) < L[rb] ? sv[rb][i] : -INFINITY;
+    }
+  };
+
+  // Softmax of one key half, in 16 steps that can ride between MFMAs:
+  // score k >> 1 on even k (P = 2^(s scale - ref) overwrites it), the bf16
+  // packing of a finished pair on odd k (word 2 kb + i/2 of row block rb's
+  // PV operand), with the lane sums of bf16(P) (the weights) and of P (the
+  // LSE) and the lane's raw maximum.
+  float mu[2], mt[2], se[2], sr[2];
+  u32x4 pcur[2];   // P operands (bf16 pairs) of the unit
+  auto sm_step = [&](int kb, float (&sv)[2][4], int k) {
+    const int j = k >> 1;
+    const int rb = j >> 2, i = j & 3;
+    if ((k & 1) == 0) {
+      mt[rb] = fmaxf(mt[rb], sv[rb][i]);
+      sv[rb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[rb][i], a.scale_log2, -mu[rb]));
+    } else if (i & 1) {
+      const uint32_t w2 = pack_bf16x2(sv[rb][i - 1], sv[rb][i]);
+      pcur[rb][2 * kb + (i >> 1)] = w2;
+      sr[rb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w2), ones, sr[rb], false);
+      se[rb] += sv[rb][i - 1] + sv[rb][i];
+    }
+  };
+
+  // O^T += V^T P^T of unit u over all 512 dims of the wave's 32 rows.
+  auto pv = [&](int u) {
+    const uint32_t ub = (uint32_t)(u % NBUF) * UB;
+    auto load_v = [&](int d) {
+      const uint32_t o0 = ub + vrow + 256u * (uint32_t)(d >> 3) + 32u * (uint32_t)((d & 7) ^ vtsw);
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sb + o0));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sb + o0 + 16384));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    bf16x8 vop[VR];
+#pragma unroll
+    for (int d = 0; d < VR - 1; ++d) vop[d] = load_v(d);
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+      if (d + VR - 1 < ND) vop[(d + VR - 1) % VR] = load_v(d + VR - 1);
+      mfma16_acc(o[d][0], vop[d % VR], __builtin_bit_cast(bf16x8, pcur[0]));
+      mfma16_acc(o[d][1], vop[d % VR], __builtin_bit_cast(bf16x8, pcur[1]));
+    }
+  };
+
+  // ---- the pipeline.  Iteration u: wait for unit u (and for every wave to
+  // be done with iteration u-1), issue the DMAs of unit u+AHEAD (into the
+  // buffer unit u-1 released at the barrier), QK(u) in two key halves with
+  // the softmax of the first half between the MFMAs of the second,
+  // softmax(u) of the second half, PV(u).
+#pragma nounroll
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+      o[d][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      o[d][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      mref[rb] = -INFINITY;
+      mtrue[rb] = -INFINITY;
+      lround[rb] = lexact[rb] = 0.f;
+    }
+    jumped = false;
+    uint32_t ops_ring = 0;   // DMA count of unit v at bits 8 (v % NBUF)
+    auto ring_set = [&](int v, int ops) {
+      const uint32_t sh = 8u * (uint32_t)(v % NBUF);
+      ops_ring = (ops_ring & ~(0xFFu << sh)) | ((uint32_t)ops << sh);
+    };
+    auto ring_get = [&](int v) { return (int)((ops_ring >> (8 * (v % NBUF))) & 0xFFu); };
+    auto stage_unit = [&](int v) {
+      const Stage st = stage_of(v);
+      if (st.valid >= UK) {   // a whole unit: one DMA per row, no per-row test
+#pragma unroll
+        for (int i = 0; i < ROWS_PW; ++i) stage_row(st, i, true);
+        ring_set(v, ROWS_PW);
+      } else {
+#pragma unroll
+        for (int i = 0; i < ROWS_PW; ++i) stage_row(st, i, false);
+        ring_set(v, stage_ops(st));
+      }
+    };
+    if (pass == 0) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const int r = min(row0 + wrow(rb), a.R - 1);
+        const uint4* qp = reinterpret_cast<const uint4*>(a.q + ((size_t)b * a.R + r) * D);
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) qreg[rb][ks] = __builtin_bit_cast(bf16x8, qp[ks * 4 + g]);
+      }
+    }
+    // units 0 .. AHEAD-1 up front.  The compiler's own loads (Q) drain with
+    // unit 0, unconditionally: the compiler does not count the staging DMAs,
+    // so any wait it placed for Q inside the key loop would also wait for
+    // the units in flight.
+    if (n_units > 0) stage_unit(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    for (int v = 1; v < AHEAD && v < n_units; ++v) stage_unit(v);
+    for (int u = 0; u < n_units; ++u) {
+      int newer = 0;   // DMA instructions issued after unit u's
+#pragma unroll
+      for (int j = 1; j < AHEAD; ++j) newer += (u + j < n_units) ? ring_get(u + j) : 0;
+      wait_vm_barrier(__builtin_amdgcn_readfirstlane(newer));   // unit u staged; iteration u-1 done everywhere
+      // the unit AHEAD past u, into the buffer unit u-1 released (one burst:
+      // each DMA issue stalls the wave while the memory pipeline is busy, and
+      // spread between the MFMAs those stalls cost more)
+      if (u + AHEAD < n_units) stage_unit(u + AHEAD);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        mt[rb] = mtrue[rb];
+        se[rb] = 0.f;
+        sr[rb] = lround[rb];
+      }
+      f32x4 s0[2], s1[2];
+      float sv0[2][4], sv1[2][4];
+      qk_half(u, 0, s0, [](int) {});
+      masked(u, 0, s0, sv0);
+      int first = __builtin_amdgcn_readfirstlane(u == 0 ? 1 : 0);
+      asm volatile("" : "+s"(first));   // opaque, so the key loop is not peeled for u == 0
+      if (first) {
+        // every row's reference for the whole item (log2 domain): the maximum
+        // over the split's first unit, or the preset of a second pass
+        qk_half(u, 1, s1, [](int) {});
+        masked(u, 1, s1, sv1);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          float m = -INFINITY;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(sv0[rb][i], sv1[rb][i]));
+          m = fmaxf(m, __shfl_xor(m, 16));
+          m = fmaxf(m, __shfl_xor(m, 32));
+          // the scale is positive, so max(s) * scale == max(s * scale)
+          mref[rb] = pass == 0 ? m * a.scale_log2 : mpreset[rb];
+          mu[rb] = (mref[rb] == -INFINITY) ? 0.f : mref[rb];   // no visible key: P = 0
+        }
+#pragma unroll
+        for (int k = 0; k < 16; ++k) sm_step(0, sv0, k);
+      } else {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) mu[rb] = (mref[rb] == -INFINITY) ? 0.f : mref[rb];
+        qk_half(u, 1, s1, [&](int ks) { sm_step(0, sv0, ks); });
+        masked(u, 1, s1, sv1);
+      }
+#pragma unroll
+      for (int k = 0; k < 16; ++k) sm_step(1, sv1, k);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        mtrue[rb] = mt[rb];
+        jumped |= mt[rb] * a.scale_log2 > mref[rb] + kMaxJump;
+        lround[rb] = sr[rb];
+        lexact[rb] += se[rb];
+      }
+      pv(u);
+    }
+    // MFMA write -> VALU write of the same accumulator (a second pass clears
+    // the tile): 24 wait states.  The clear sits behind the branch below.
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    if (pass == 1) break;
+    if (tid == 0) *sm_redo = 0;
+    __syncthreads();   // every wave is done with the buffers and has read the flag's old value
+    if (__any(jumped) && lane == 0) *sm_redo = 1;
+    __syncthreads();
+    if (*sm_redo == 0) break;
+    // second pass: every row's reference is its true maximum over the item
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      float m = mtrue[rb] * a.scale_log2;
+      m = fmaxf(m, __shfl_xor(m, 16));
+      mpreset[rb] = fmaxf(m, __shfl_xor(m, 32));
+    }
+  }
+  // accumulators of the last 8 PV MFMAs: 8 more wait states each, in write order
+#pragma unroll
+  for (int d = ND - 4; d < ND; ++d) {
+    settle_acc(o[d][0]);
+    settle_acc(o[d][1]);
+  }
+
+  // ---- finalize: row sums over the four lane groups; (-inf, 0) for rows
+  // without a visible key; the scaled bf16 rows are staged in LDS at a pitch
+  // of SPITCH bytes and leave as whole 1 KiB rows
+  float lr[2], le[2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    lr[rb] = lround[rb] + __shfl_xor(lround[rb], 16);
+    lr[rb] += __shfl_xor(lr[rb], 32);
+    le[rb] = lexact[rb] + __shfl_xor(lexact[rb], 16);
+    le[rb] += __shfl_xor(le[rb], 32);
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // every wave is done with the key buffers
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int row = wrow(rb);
+    const bool empty = !(lr[rb] > 0.f);   // a visible key contributes P >= 1 (its max set the reference)
+    const float inv = empty ? 0.f : __builtin_amdgcn_rcpf(lr[rb]);
+    lds_u8* const rowp = sb + row * SPITCH + 8 * g;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+      const f32x4 v = o[d][rb] * inv;
+      *(lds_u32x2*)(rowp + 32 * d) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    }
+    if (g == 0) {
+      st_lr[row] = lr[rb];
+      if (row0 + row < a.R) {
+        const size_t row_g = (size_t)b * a.R + row0 + row;
+        const float l = empty ? -INFINITY : (mref[rb] + __builtin_amdgcn_logf(le[rb])) * kLn2;
+        if (a.direct) a.lse[row_g] = l;
+        else a.part_lse[(size_t)s * a.B * a.R + row_g] = l;
+      }
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's rows are staged (it stores only its own)
+  uint16_t* const dst0 = a.direct ? a.out_lat + ((size_t)b * a.R + row0) * D
+                                  : a.part_o + ((size_t)s * a.B * a.R + (size_t)b * a.R + row0) * D;
+  bool live = false;   // lane j: is row 32 w + j stored
+  if (lane < 32 && 32 * w + lane < rows_here) live = a.direct || st_lr[32 * w + lane] > 0.f;
+  const uint64_t live_mask = __ballot(live);
+#pragma unroll 4
+  for (int j = 0; j < 32; ++j) {
+    if (!((live_mask >> j) & 1)) continue;
+    const int row = 32 * w + j;
+    const u32x4 rv = *(const lds_u32x4*)(sb + row * SPITCH + 16 * lane);
+    if (a.l2_partials && !a.direct)
+      *reinterpret_cast<u32x4*>(dst0 + (size_t)row * D + 8 * lane) = rv;
+    else
+      st_stream16_asm(dst0 + (size_t)row * D + 8 * lane, rv);
+  }
+  };
+
+  // ---- the work items of this workgroup.
+  //   per-tile splits (!balanced): one item, (request, split, row tile) from
+  //     the grid position.
+  //   balanced chunks: request b has U_b = ceil(n_b / 32) units (n_b its
+  //     largest bound); the requests' units laid end to end are cut into G
+  //     chunks of C units, C = max(ceil(U / groups), chunk_min).  A group of
+  //     row_tiles workgroups on one XCD (one per row tile, so the tiles of a
+  //     request stream the same pages through one L2 together) takes chunk
+  //     grp: for every request the chunk touches, its rows over those units,
+  //     into partial slot grp - (first chunk of the request).  chunk_min keeps
+  //     the chunks of one request at most S.  The group holding a request's
+  //     last unit sets the LSEs of its unused slots to -inf; a request with no
+  //     visible key gets -inf in every slot from the group owning its
+  //     position.
+  int rt = 0, grp = 0, C = 1, G = 1, lo = 0, hi = 0, b = 0, b_end = 0;
+  __attribute__((address_space(3))) int32_t* s_start =
+      (__attribute__((address_space(3))) int32_t*)(sp + 2048);   // request starts, past bounds and row overflow
+  if (!a.balanced) {
+    int id = logical_item(blockIdx.x, a.B * a.S, a.row_tiles, dealt_layout(a.row_tiles));
+    if (id < 0) return;
+    rt = id % a.row_tiles;
+    id /= a.row_tiles;
+    b = id / a.S;
+    grp = id % a.S;
+    b_end = b + 1;
+  } else {
+    const int gpx = 32 / a.row_tiles;                 // whole groups per XCD
+    const int xcd = blockIdx.x % mla::kNumXCDs, pos = blockIdx.x / mla::kNumXCDs;
+    rt = pos % a.row_tiles;
+    if (pos / a.row_tiles >= gpx) return;
+    const int n_groups = mla::kNumXCDs * gpx;
+    grp = (pos / a.row_tiles) * mla::kNumXCDs + xcd;
+    {   // exclusive prefix sums of U_b
+      constexpr int PER = 8;   // requests per thread (B <= 2048)
+      int cnt[PER];
+      int sum = 0;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int bq = tid * PER + j;
+        int nb = 0;
+        if (bq < a.B)
+          for (int t = 0; t < a.T; ++t) nb = max(nb, clampi(a.bounds[(size_t)bq * a.T + t], 0, max_keys));
+        cnt[j] = (nb + UK - 1) / UK;
+        sum += cnt[j];
+      }
+      int incl = sum;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off);
+        if (lane >= off) incl += v;
+      }
+      __attribute__((address_space(3))) int32_t* wsum = s_start + 2044;   // [4], past s_start[0 .. B] (B <= 2000)
+      if (lane == 63) wsum[w] = incl;
+      __syncthreads();
+      int base = incl - sum;
+      for (int k = 0; k < w; ++k) base += wsum[k];
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int bq = tid * PER + j;
+        if (bq < a.B) s_start[bq] = base;
+        base += cnt[j];
+      }
+      if (tid == 255) s_start[a.B] = base;
+      __syncthreads();
+    }
+    const int U = __builtin_amdgcn_readfirstlane(s_start[a.B]);
+    C = max((U + n_groups - 1) / n_groups, a.chunk_min);
+    G = max(1, (U + C - 1) / C);
+    if (grp >= G) return;
+    lo = grp * C;
+    hi = grp == G - 1 ? INT_MAX : lo + C;
+    // first request with units past lo, or starting at or after lo
+    int bn = a.B;
+    while (b < bn) {
+      const int mid = (b + bn) >> 1;
+      const int s1 = __builtin_amdgcn_readfirstlane(s_start[mid + 1]);
+      const int s0 = __builtin_amdgcn_readfirstlane(s_start[mid]);
+      if (s1 > lo || s0 >= lo) bn = mid;
+      else b = mid + 1;
+    }
+    b_end = a.B;
+  }
+  auto clear_slots = [&](int bb, int from) {   // lse = -inf in slots from .. S-1 of tile (bb, rt)
+    const int row0 = rt * RT, rows_here = min(RT, a.R - row0);
+    for (int i = tid; i < (a.S - from) * rows_here; i += kThreads) {
+      const int sl = from + i / rows_here, r = i % rows_here;
+      a.part_lse[(size_t)sl * a.B * a.R + (size_t)bb * a.R + row0 + r] = -INFINITY;
+    }
+  };
+  for (; b < b_end; ++b) {
+    int slot = grp, ua = 0, ub = 0, tail = a.S;
+    if (a.balanced) {
+      const int st = __builtin_amdgcn_readfirstlane(s_start[b]);
+      if (st >= hi) break;
+      const int Ub = __builtin_amdgcn_readfirstlane(s_start[b + 1]) - st;
+      if (Ub == 0) {
+        if (min(st / C, G - 1) == grp) clear_slots(b, 0);
+        continue;
+      }
+      slot = grp - st / C;
+      ua = max(lo - st, 0);
+      ub = min(hi - st, Ub);
+      if (hi - st >= Ub) tail = slot + 1;   // this group holds the request's last unit
+    }
+    run_item(b, rt, slot, ua, ub, !a.balanced);
+    if (tail < a.S) clear_slots(b, tail);
+  }
+}
+
 // LSE merge of the S partials of one row, computed by one wave (lane owns
 // dims 8*lane .. 8*lane+7).  Returns the row's lse; (-inf, 0) when no split
 // saw a key.  A partial whose LSE is -inf gets weight 0 through a select, so
@@ -1429,7 +2012,8 @@ int ensure_device() {
                             reinterpret_cast<const void*>(attn_kernel<2, false>),
                             reinterpret_cast<const void*>(attn_kernel<0, true>),
                             reinterpret_cast<const void*>(attn_kernel<1, true>),
-                            reinterpret_cast<const void*>(attn_kernel<2, true>)};
+                            reinterpret_cast<const void*>(attn_kernel<2, true>),
+                            reinterpret_cast<const void*>(attn_rows_kernel)};
       bool fail = false;
       for (const void* f : attn)
         fail |= hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kAttnSmemBytes) !=
@@ -1461,7 +2045,8 @@ int ensure_device() {
 // same XCD.
 bool partials_stay_in_l2(const mla_verify_params* p, const mla::Plan& pl) {
   const size_t part_bytes_per_xcd = (size_t)pl.splits * p->batch * pl.rows * D * 2 / mla::kNumXCDs;
-  return pl.splits > 1 && !dealt_layout(pl.row_tiles) && part_bytes_per_xcd <= mla::kL2BytesPerXCD / 4;
+  return pl.splits > 1 && !pl.balanced && !dealt_layout(pl.row_tiles) &&
+         part_bytes_per_xcd <= mla::kL2BytesPerXCD / 4;
 }
 
 // Launch the attention kernel.  With partials, part_o / part_lse receive the
@@ -1489,6 +2074,8 @@ int run_attention(const mla_verify_params* p, const mla::Plan& pl, const mla_bf1
   a.kv_scale = p->kv_dtype == MLA_KV_FP8_E4M3 ? p->kv_scale : 1.0f;
   a.scale_log2 = p->sm_scale * a.kv_scale * kLog2e;
   a.min_split_pages = pl.min_split_pages;
+  a.balanced = pl.balanced ? 1 : 0;
+  a.chunk_min = pl.chunk_min;
   a.direct = partials ? 0 : 1;
   if (partials) {
     a.part_o = part_o;
@@ -1498,8 +2085,9 @@ int run_attention(const mla_verify_params* p, const mla::Plan& pl, const mla_bf1
     a.lse = lse;
   }
   const size_t groups = (size_t)p->batch * pl.splits;
-  const unsigned grid =
-      (unsigned)((groups + mla::kNumXCDs - 1) / mla::kNumXCDs * mla::kNumXCDs * pl.row_tiles);
+  // balanced chunks: one workgroup per CU (groups of row_tiles on one XCD)
+  const unsigned grid = pl.balanced ? (unsigned)mla::kNumCUs
+      : (unsigned)((groups + mla::kNumXCDs - 1) / mla::kNumXCDs * mla::kNumXCDs * pl.row_tiles);
   const int mode = pl.shape.mode;
   const bool kv8 = p->kv_dtype == MLA_KV_FP8_E4M3;
   auto go = [&](auto kernel) {
@@ -1509,6 +2097,7 @@ int run_attention(const mla_verify_params* p, const mla::Plan& pl, const mla_bf1
   if (mode == 0) return kv8 ? go(attn_kernel<0, true>) : go(attn_kernel<0, false>);
   if (mode == 1) return kv8 ? go(attn_kernel<1, true>) : go(attn_kernel<1, false>);
   if (mode == 2) return kv8 ? go(attn_kernel<2, true>) : go(attn_kernel<2, false>);
+  if (mode == 3 && !kv8) return go(attn_rows_kernel);
   return MLA_ERR_SHAPE;
 }
 

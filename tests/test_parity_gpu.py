@@ -369,6 +369,39 @@ def library_split_count(n_keys, num_splits, max_pages):
     return min(num_splits, max(1, -(-n_pg // m)))
 
 
+def balanced_chunks(x, splits, tile):
+    """Key ranges of every partial slot under the balanced-chunk partition the
+    header documents for 128-row tiles on a bf16 cache (split count >= 2):
+    request b has U_b = ceil(n_b / 32) units, n_b its largest bound; the
+    requests' units end to end are cut into chunks of C = max(ceil(U / g),
+    ceil(2 P / (S - 1))) units, g = 8 * floor(32 / row tiles); slot j of
+    request b is its part of chunk floor(start_b / C) + j.  Returns
+    {b: [(k0, k1), ...]} in request keys (before each tile's own clip)."""
+    b_n, t, h = x.shape
+    max_pages = x.block_table.shape[1]
+    n_b = np.clip(x.kv_bounds, 0, max_pages * 64).max(axis=1)
+    units = [-(-int(n) // 32) for n in n_b]
+    starts = np.concatenate([[0], np.cumsum(units)]).astype(int)
+    total = int(starts[-1])
+    row_tiles = -(-(t * h) // tile)
+    groups = 8 * (32 // row_tiles)
+    c = max(-(-total // groups), -(-(2 * max_pages) // (splits - 1)))
+    g_used = max(1, -(-total // c))
+    out = {}
+    for bi in range(b_n):
+        st, ub = int(starts[bi]), units[bi]
+        rng = []
+        if ub > 0:
+            q0, q1 = st // c, (st + ub - 1) // c
+            for q in range(q0, q1 + 1):
+                lo = q * c
+                hi = float("inf") if q == g_used - 1 else lo + c
+                rng.append((max(lo, st) - st, min(hi, st + ub) - st))
+        assert len(rng) <= splits
+        out[bi] = [(a * 32, b_ * 32) for a, b_ in rng]
+    return out
+
+
 def check_partials_and_combine(x, splits, tile_rows=0):
     """mla_verify_attn_partials: split s of a row is attention over the keys of
     chunk s of its row tile's partition (clipped to the row's token bound);
@@ -396,14 +429,20 @@ def check_partials_and_combine(x, splits, tile_rows=0):
     max_pages = x.block_table.shape[1]
     want_o, want_l, got_o, got_l = [], [], [], []
     n_empty = 0
+    balanced = tile == 128 and getattr(x, "kv_dtype", "bf16") == "bf16" and splits >= 2 and b <= 2000
+    bal = balanced_chunks(x, splits, tile) if balanced else None
     for bi in range(b):
         c_b, n_b = oracle.request_keys(x.pool, x.block_table, x.kv_bounds, bi)
         for r0 in range(0, t * h, tile):
             rows = range(r0, min(r0 + tile, t * h))
             # the tile sees the keys up to its own largest bound
             n_tile = max(oracle.token_bound(x.kv_bounds, bi, r // h, n_b) for r in rows)
-            used = library_split_count(n_tile, splits, max_pages)
-            chunks = oracle.split_pages(n_tile, used) + [(n_tile, n_tile)] * (splits - used)
+            if balanced:
+                chunks = [(min(k0, n_tile), min(k1, n_tile)) for k0, k1 in bal[bi]]
+                chunks += [(n_tile, n_tile)] * (splits - len(chunks))
+            else:
+                used = library_split_count(n_tile, splits, max_pages)
+                chunks = oracle.split_pages(n_tile, used) + [(n_tile, n_tile)] * (splits - used)
             for s, (k0, k1) in enumerate(chunks):
                 for r in rows:
                     L = oracle.token_bound(x.kv_bounds, bi, r // h, n_b)
@@ -427,6 +466,23 @@ def check_partials_and_combine(x, splits, tile_rows=0):
 def test_partials_match_oracle_chunks_and_combine_matches_call(cfg, splits, tile):
     log(f"partials + combine: config {cfg} sharp, S={splits}, tile {tile}")
     check_partials_and_combine(make_config(cfg, sharp=True), splits, tile)
+
+
+@pytest.mark.parametrize("splits", [2, 3, 8])
+def test_partials_balanced_chunks_on_128_row_tiles(splits):
+    """128-row tiles on a bf16 cache (64 heads x 8 tokens: four tiles per
+    request): the balanced-chunk partition, with a request that sees
+    nothing, a request whose later tokens see nothing (a tile shorter than
+    the request), lengths on and off unit and page edges, and forced split
+    counts that bind the chunk size (2, 3) or not (8)."""
+    log(f"partials, balanced chunks, S={splits}")
+    ctx = np.array([2000, 0, 33, 1500, 64, 4100, 95, 1])
+    bounds = (ctx[:, None] - 7 + np.arange(8)[None, :]).clip(0).astype(np.int32)
+    bounds[3, 2:] = 0                      # tiles 1..3 of request 3 see nothing
+    bounds[6, :4] = 0
+    x = build_inputs(batch=len(ctx), heads=64, q_len=8, ctx=ctx, bounds=bounds, seed=77,
+                     latent_q=True, q_scale=1536.0)
+    check_partials_and_combine(x, splits, tile_rows=128)
 
 
 def test_partials_ragged_batch_takes_fewer_splits_for_short_requests():
