@@ -234,24 +234,50 @@ def traffic_path(config, kv="bf16"):
     return os.path.join(ROOT, "profiles", f"traffic_config{config}{suffix}.json")
 
 
+# the kernels of one call, by a part of their names
+CALL_KERNELS = {"attention": "attn_", "combine": "combine_kernel", "gated_epilogue": "gated_epilogue"}
+
+
+def _median(vals):
+    vals = sorted(vals)
+    return vals[len(vals) // 2]
+
+
 def pmc_report(directory, config, kv="bf16"):
-    """Calibrated HBM traffic of the attention kernel from two counter runs."""
-    out = {"config": config, "kernel_source_sha": kernel_source_hash()}
+    """Calibrated HBM traffic of the call's kernels from two counter runs
+    (FETCH_SIZE in DIR/fetch, WRITE_SIZE in DIR/write) and, when DIR/mfma
+    holds a run of SQ_VALU_MFMA_BUSY_CYCLES + GRBM_GUI_ACTIVE, the attention
+    kernel's MFMA busy share.  Values are medians over the dispatches of each
+    kernel."""
+    out = {"config": config, "kernel_source_sha": kernel_source_hash(), "kernels": {}}
     for counter, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
         rows = _counter_rows(os.path.join(directory, sub), counter)
         copy = _per_dispatch(rows, "copy") or _per_dispatch(rows, "elementwise")
-        attn = _per_dispatch(rows, "attn_")
-        if not copy or not attn:
+        if not copy or not _per_dispatch(rows, CALL_KERNELS["attention"]):
             raise SystemExit(f"{counter}: missing copy probe or attention dispatches in {sub}")
         copy_kib = max(copy.values())          # the 1 GiB probe is the largest copy
         factor = COPY_PROBE_BYTES / (copy_kib * 1024.0)
-        vals = sorted(attn.values())
-        med = vals[len(vals) // 2]
-        out[counter.lower()] = {"raw_kib_per_dispatch": med, "copy_probe_raw_kib": copy_kib,
-                                "factor": round(factor, 4),
-                                "bytes_per_dispatch": round(med * 1024.0 * factor)}
-    out["traffic_bytes"] = out["fetch_size"]["bytes_per_dispatch"] + \
-        out["write_size"]["bytes_per_dispatch"]
+        out[counter.lower() + "_copy_probe"] = {"raw_kib": copy_kib, "factor": round(factor, 4)}
+        for name, part in CALL_KERNELS.items():
+            vals = _per_dispatch(rows, part)
+            if not vals:
+                continue
+            med = _median(vals.values())
+            out["kernels"].setdefault(name, {})[counter.lower()] = {
+                "raw_kib_per_dispatch": med, "bytes_per_dispatch": round(med * 1024.0 * factor)}
+    for k in out["kernels"].values():
+        k["traffic_bytes"] = k["fetch_size"]["bytes_per_dispatch"] + k["write_size"]["bytes_per_dispatch"]
+    out["traffic_bytes"] = out["kernels"]["attention"]["traffic_bytes"]
+    out["call_traffic_bytes"] = sum(k["traffic_bytes"] for k in out["kernels"].values())
+    mdir = os.path.join(directory, "mfma")
+    if os.path.isdir(mdir):
+        busy = _per_dispatch(_counter_rows(mdir, "SQ_VALU_MFMA_BUSY_CYCLES"), CALL_KERNELS["attention"])
+        active = _per_dispatch(_counter_rows(mdir, "GRBM_GUI_ACTIVE"), CALL_KERNELS["attention"])
+        # busy cycles are summed over the 1024 SIMDs, GRBM_GUI_ACTIVE over the
+        # 8 XCDs (the same clock on each)
+        pct = [100.0 * busy[d] / (active[d] / 8.0 * 1024.0) for d in busy if active.get(d)]
+        if pct:
+            out["attention_mfma_busy_pct"] = round(_median(pct), 2)
     path = traffic_path(config, kv)
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
@@ -259,15 +285,16 @@ def pmc_report(directory, config, kv="bf16"):
 
 
 def recorded_traffic(config, kv="bf16"):
+    """The counter record of this workload, if it was taken on this kernel source."""
     path = traffic_path(config, kv)
     try:
         with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
-        return None
+        return {}
     if rec.get("kernel_source_sha") != kernel_source_hash():
-        return None        # counted on another version of the kernel
-    return rec.get("traffic_bytes")
+        return {}        # counted on another version of the kernel
+    return rec
 
 
 # --------------------------------------------------------------- timing
@@ -523,6 +550,7 @@ def measure(cfg, args, steps, warmup, n_samples, lib, timer, with_kv_updates):
     kv_us = kv_update_timings(x, pools, bt, timer, lib, torch, np) if (with_kv_updates and not fp8) else {}
 
     alg = algorithmic(x, gated, kernel_writes_output=attn_alone_is_call)
+    counters = recorded_traffic(cfg, args.kv)
     k_roof = roof(alg["kernel_bytes"], alg["kernel_flops"], kms * 1e-3)
     c_roof = roof(alg["bytes"], alg["flops"], ms * 1e-3)
     tokens = b * t
@@ -542,7 +570,9 @@ def measure(cfg, args, steps, warmup, n_samples, lib, timer, with_kv_updates):
         "kernel_bytes": alg["kernel_bytes"], "kernel_flops": alg["kernel_flops"],
         "kernel": {**k_roof, "kv_gbs": round(alg["kv_bytes"] / (kms * 1e-3) / 1e9, 1)},
         "call": {**c_roof, "kv_gbs": round(alg["kv_bytes"] / (ms * 1e-3) / 1e9, 1)},
-        "traffic": recorded_traffic(cfg, args.kv),
+        "traffic": counters.get("traffic_bytes"),
+        "call_traffic": counters.get("call_traffic_bytes"),
+        "mfma_busy_pct": counters.get("attention_mfma_busy_pct"),
         **kv_us,
     }
     del pools, ws, part_o, part_lse, q_lat
@@ -624,10 +654,10 @@ def main():
                     "unit": "TFLOP/s", "frac": k["mfma_frac"], "traffic": head["traffic"]}
     if c["bound"] == "hbm":
         roofline_call = {"bound": "hbm", "achieved": c["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": c["hbm_frac"]}
+                         "frac": c["hbm_frac"], "traffic": head["call_traffic"]}
     else:
         roofline_call = {"bound": "mfma", "achieved": c["tflops"], "peak": MFMA_BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": c["mfma_frac"]}
+                         "unit": "TFLOP/s", "frac": c["mfma_frac"], "traffic": head["call_traffic"]}
     cfg_out = {k2: head[k2] for k2 in ("workload", "batch", "heads", "q_len", "kv_cache",
                                        "num_splits", "tile_rows", "gated", "cache", "bounds",
                                        "scores", "launch")}

@@ -37,6 +37,7 @@
 // The paged-cache updates (KV append, trim) live in mla_kv_update.hip.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
@@ -1698,162 +1699,228 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint16_t* __res
   if (lane == 0) lse[row] = l;
 }
 
-// Gated epilogue: one workgroup per (head h, 16 (b, t) rows).
-//   merge   wave w owns tile rows w, w + 4, w + 8, w + 12 and merges RB of
-//           them at a time: one round trip fetches the S LSEs of the RB rows
-//           (LPR = 64 / RB lanes per row, one split per lane), the weights
-//           exp(lse_s - max) follow, and a second round trip fetches only the
-//           partials with a nonzero weight (at most 16 in flight per lane);
-//           the bf16 o_lat rows go to an LDS tile, lse and the optional
-//           out_latent to memory.  Rows with no visible key give (-inf, 0).
-//   W_UV    wave w computes out dims 32 w .. +31 of all 16 rows on MFMA
-//           (A = o_lat tile from LDS, B = W_UV[h] rows straight from memory),
-//           then multiplies by sigmoid(gate).
-//   WPRE    (grids that fit one workgroup per CU, i.e. small batches, where
-//           the latency of each step is the cost) W_UV[h] is staged into LDS
-//           by DMA at the start -- each wave its own 32 dims, 1 KiB rows with
-//           16-byte chunks XOR-swizzled by the dim's low bits -- so it lands
-//           while the merge runs, and the MFMA reads it from LDS.
-constexpr int kWuvLdsBytes = DV * D * 2;   // W_UV[h]: 128 dims x 512 bf16
-template <int RB, bool WPRE>
-__global__ __launch_bounds__(kThreads, WPRE ? 1 : 3) void gated_epilogue_kernel(
+// Gated epilogue: workgroups of 8 waves, each owning one head h and a run of
+// consecutive 64-row blocks of it ((b, t) rows 64 blk .. +63).
+//   W_UV   wave w holds the MFMA B operand of out dims 16 w .. +15 of W_UV[h]
+//          in registers (16 KiB per wave), loaded once per workgroup.
+//   merge  wave w owns tile rows w, w + 8, ..., w + 56 of a block and merges
+//          them in units of G = 64 / LPR rows (LPR >= S lanes per row): one
+//          load of the unit's LSEs (one split per lane), the weights
+//          exp(lse_s - max), then only the (row, split) pairs with a nonzero
+//          weight are fetched, in row order, 16 per lane at a time.  A row's
+//          normalised sum goes to the LDS tile as bf16 (and to out_latent),
+//          its lse to memory; rows with no visible key give (-inf, 0).
+//   W_UV   out[64 rows][16 dims of wave w] = tile . W_UV[h]^T on MFMA (four
+//          independent 16-row accumulators), times sigmoid(gate).
+// Software pipeline: the LSEs of unit u + 2 and the pairs of unit u + 1 are
+// in flight while unit u is summed and its block goes through the MFMAs.
+// Every global load is unconditional, from a clamped or repeated address,
+// so that the count of loads in flight is static and the compiler's waits
+// name exactly the loads they need.
+constexpr int kEpiRows = 64;
+constexpr int kEpiThreads = 512;
+constexpr int kEpiPairs = 16;   // pair loads in flight per lane
+// v from lane `src` (wave-uniform index)
+__device__ __forceinline__ float lane_f32(float v, int src) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), src));
+}
+template <int LPR>
+__global__ __launch_bounds__(kEpiThreads, 1) void gated_epilogue_kernel(
     const uint16_t* __restrict__ part_o, const float* __restrict__ part_lse,
     const uint16_t* __restrict__ w_uv, const uint16_t* __restrict__ gate,
     uint16_t* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ out_latent,
-    int BT, int H, int S) {
-  constexpr int LPR = 64 / RB;   // lanes per row for the LSEs: S <= LPR
-  constexpr int CHK = 16 / RB;   // partial loads in flight per row (16 per lane: 3 workgroups fit a CU)
-  __shared__ uint4 tile[16 * 64];   // 16 rows x 64 chunks of 16 bytes, chunk c of row r at r*64 + (c ^ (r & 15))
-  extern __shared__ uint4 wuv_lds[];   // WPRE: W_UV[h], dim d's chunk c at d*64 + (c ^ (d & 15))
+    int BT, int H, int S, int blocks_per_wg) {
+  constexpr int G = 64 / LPR;             // rows per unit
+  constexpr int NG = 8 / G;               // units per block and wave
+  constexpr uint64_t kSeg = LPR == 64 ? ~0ull : ((1ull << LPR) - 1);
+  // 64 rows x 64 chunks of 16 bytes; chunk c of row r at r*64 + (c ^ (r & 15))
+  __shared__ uint4 tile[kEpiRows * 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, i16 = lane & 15;
   const int h = blockIdx.x % H;
-  const int rr0 = (blockIdx.x / H) * 16;
+  const int n_blk = (BT + kEpiRows - 1) / kEpiRows;
+  const int blk0 = (blockIdx.x / H) * blocks_per_wg;
+  const int n_units = (min(n_blk, blk0 + blocks_per_wg) - blk0) * NG;
+  if (n_units <= 0) return;   // uniform
   const size_t rows = (size_t)BT * H;
-  const uint16_t* wh = w_uv + (size_t)h * DV * D;
-  if constexpr (WPRE) {
-    // dims 32 wave .. +31 of W_UV[h]: one 1 KiB row per DMA; lane l fetches
-    // chunk l ^ (d & 15), so chunk c lands at position c ^ (d & 15)
-    const uint32_t base = (uint32_t)(uintptr_t)wuv_lds;
-#pragma unroll 8
-    for (int i = 0; i < 32; ++i) {
-      const int d = 32 * wave + i;
-      dma_row16(wh + (size_t)d * D, 16u * (uint32_t)(lane ^ (d & 15)), base + (uint32_t)d * 1024u);
-    }
-  }
+  const int q = lane / LPR, j = lane % LPR;   // (row of the unit, split) of this lane's LSE
 
-  // gate values of this lane's outputs: C[row 4g + i][dim 32 wave + 16 nt + i16]
-  float gv[2][4];
+  // (b, t) row of row qq of unit u
+  auto row_of = [&](int u, int qq) { return (blk0 + u / NG) * kEpiRows + wave + 8 * ((u % NG) * G + qq); };
+  auto tile_row = [&](int u, int qq) { return wave + 8 * ((u % NG) * G + qq); };
+  // this lane's LSE of unit u as loaded (clamped address; units past the
+  // end read the last one), and the -inf to add where the lane holds no
+  // (row, split): added when the weights are formed rather than selected at
+  // the load, which the compiler would turn into a branch around the load
+  // or a wait for it (a stored lse is never +inf)
+  auto lse_load = [&](int u) {
+    const int rr = row_of(min(u, n_units - 1), q);
+    return part_lse[(size_t)min(j, S - 1) * rows + (size_t)min(rr, BT - 1) * H + h];
+  };
+  auto lse_mask = [&](int u) { return (row_of(u, q) < BT && j < S) ? 0.f : -INFINITY; };
+  // gate of this lane's outputs of block b: row 16 rb + 4 g + i, dim 16
+  // wave + i16 (loaded after the stores of the block before)
+  uint32_t gb[4][4];
+  auto load_gates = [&](int b) {
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
+    for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rr = rr0 + 4 * g + i;
-      gv[nt][i] = rr < BT ? bf16_to_f32(gate[((size_t)rr * H + h) * DV + 32 * wave + 16 * nt + i16]) : 0.f;
-    }
+      for (int i = 0; i < 4; ++i) {
+        const int rr = min((blk0 + b) * kEpiRows + 16 * rb + 4 * g + i, BT - 1);
+        gb[rb][i] = gate[((size_t)rr * H + h) * DV + 16 * wave + i16];
+      }
+  };
 
-  const int qq = lane / LPR, j = lane % LPR;   // (row of the batch, split) of this lane's LSE
-#pragma unroll 1
-  for (int q0 = 0; q0 < 4; q0 += RB) {
-    // ---- LSEs and weights of rows w + 4 (q0 + qq)
-    const int lr_l = wave + 4 * (q0 + qq);
-    const int rr_l = rr0 + lr_l;
-    const size_t row_l = (size_t)rr_l * H + h;
-    const float l = (rr_l < BT && j < S) ? part_lse[(size_t)j * rows + row_l] : -INFINITY;
-    float mx = l;
+  // per unit: the LSE state and the pairs in flight
+  float l_raw = lse_load(0);
+  float mx, wl, total;
+  uint64_t m_all, m_rest;
+  uint4 v[kEpiPairs];
+  int bits[kEpiPairs];
+  auto weights = [&](int u) {
+    const float l = l_raw + lse_mask(u);
+    mx = l;
 #pragma unroll
     for (int off = LPR / 2; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-    const float wl = (l == -INFINITY) ? 0.f : expf(l - mx);
-    float total = wl;
+    wl = (l == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((l - mx) * kLog2e);
+    total = wl;
 #pragma unroll
     for (int off = LPR / 2; off >= 1; off >>= 1) total += __shfl_xor(total, off);
-    // ---- weighted sum of the partials with a nonzero weight
-    float acc[RB][8];
+    m_all = __ballot(wl > 0.f);   // bit q * LPR + j: pair (row q, split j) has weight
+    m_rest = m_all;
+  };
+  // the next (up to) kEpiPairs pairs of unit u; past the last pair a load
+  // repeats the previous address and its bits entry is -1
+  auto issue = [&](int u) {
+    // (branch free: a branch around the address would make the compiler
+    // wait for each load at the join)
+    size_t off = 0;   // element offset of the pair's row, uniform
 #pragma unroll
-    for (int q = 0; q < RB; ++q)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[q][e] = 0.f;
-    for (int c0 = 0; c0 < S; c0 += CHK) {
-      auto weight = [&](int q, int k) {   // weight of split c0 + k for batch row q
-        const int jj = c0 + k;
-        return jj < S ? __shfl(wl, q * LPR + (jj & (LPR - 1))) : 0.f;
-      };
-      uint4 v[RB][CHK];
-#pragma unroll
-      for (int q = 0; q < RB; ++q) {
-        const size_t row = (size_t)(rr0 + wave + 4 * (q0 + q)) * H + h;
-#pragma unroll
-        for (int k = 0; k < CHK; ++k) {
-          v[q][k] = make_uint4(0, 0, 0, 0);
-          if (weight(q, k) > 0.f)   // wave-uniform: a split the row saw no key of is never read
-            v[q][k] = ld_stream16(part_o + ((size_t)(c0 + k) * rows + row) * D + lane * 8);
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < RB; ++q)
-#pragma unroll
-        for (int k = 0; k < CHK; ++k) {
-          const float ws = weight(q, k);
-          const uint32_t wd[4] = {v[q][k].x, v[q][k].y, v[q][k].z, v[q][k].w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc[q][2 * e] += ws * bf16_to_f32(wd[e] & 0xFFFFu);
-            acc[q][2 * e + 1] += ws * bf16_to_f32(wd[e] >> 16);
-          }
-        }
+    for (int k = 0; k < kEpiPairs; ++k) {
+      const int bit = __builtin_ffsll((long long)m_rest) - 1;   // -1: no pair left
+      m_rest &= m_rest - 1;
+      bits[k] = bit;
+      const int b2 = max(bit, 0);
+      const size_t o2 = ((size_t)(b2 % LPR) * rows + (size_t)row_of(u, b2 / LPR) * H + h) * D;
+      off = bit >= 0 ? o2 : off;
+      v[k] = ld_stream16(part_o + off + lane * 8);
     }
-    // ---- rows out: LDS tile (bf16), lse, optional out_latent
-#pragma unroll
-    for (int q = 0; q < RB; ++q) {
-      const int lr = wave + 4 * (q0 + q);
-      const int rr = rr0 + lr;
-      const float tq = __shfl(total, q * LPR);
-      const float mq = __shfl(mx, q * LPR);
-      uint4 wv = make_uint4(0, 0, 0, 0);
-      if (rr < BT && tq > 0.f) {
-        const float inv = 1.f / tq;
-        wv.x = pack_bf16x2(acc[q][0] * inv, acc[q][1] * inv);
-        wv.y = pack_bf16x2(acc[q][2] * inv, acc[q][3] * inv);
-        wv.z = pack_bf16x2(acc[q][4] * inv, acc[q][5] * inv);
-        wv.w = pack_bf16x2(acc[q][6] * inv, acc[q][7] * inv);
-      }
-      tile[lr * 64 + (lane ^ (lr & 15))] = wv;
-      if (rr < BT) {
-        const size_t row = (size_t)rr * H + h;
-        if (out_latent) st_stream16(out_latent + row * D + lane * 8, wv);
-        if (lane == 0) lse[row] = tq > 0.f ? mq + logf(tq) : -INFINITY;
-      }
-    }
-  }
-  if constexpr (WPRE) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's W_UV rows landed
-  __syncthreads();
+  };
 
-  // ---- out[16 rows][32 dims of this wave] = o_lat[16][512] . W_UV[h][dims][512]^T
-  f32x4 acc2[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll 4
-  for (int ks = 0; ks < 16; ++ks) {
-    const bf16x8 av = __builtin_bit_cast(bf16x8, tile[i16 * 64 + ((4 * ks + g) ^ i16)]);
+  // prologue: the W_UV operand and the gates of block 0 go out behind the
+  // LSEs of unit 0 (the scheduling barrier keeps them ahead of the wait for
+  // those LSEs), then the pairs of unit 0 and the LSEs of unit 1
+  const uint16_t* wd = w_uv + ((size_t)h * DV + 16 * wave + i16) * D + 8 * g;
+  uint4 wreg[16];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int d = 32 * wave + 16 * nt + i16;
-      uint4 bv;
-      if constexpr (WPRE)
-        bv = wuv_lds[d * 64 + ((4 * ks + g) ^ (d & 15))];
-      else
-        bv = *reinterpret_cast<const uint4*>(wh + (size_t)d * D + ks * 32 + 8 * g);
-      acc2[nt] = mfma16(av, __builtin_bit_cast(bf16x8, bv), acc2[nt]);
+  for (int ks = 0; ks < 16; ++ks) wreg[ks] = *reinterpret_cast<const uint4*>(wd + ks * 32);
+  load_gates(0);
+  __builtin_amdgcn_sched_barrier(0);
+  weights(0);
+  issue(0);
+  l_raw = lse_load(1);
+
+#pragma unroll 1
+  for (int u = 0; u < n_units; ++u) {
+    // ---- rows of unit u without a visible key: (-inf, 0).  Lane qq
+    // collects row qq's lse; the unit's LSEs go out in one store after the
+    // sums (a store per row would hold its data register, and the compiler
+    // waits for the store before that register is reused)
+    float lse_lane = -INFINITY;
+#pragma unroll
+    for (int qq = 0; qq < G; ++qq) {
+      if (((m_all >> (qq * LPR)) & kSeg) != 0) continue;
+      const int lr = tile_row(u, qq);
+      const int rr = row_of(u, qq);
+      tile[lr * 64 + (lane ^ (lr & 15))] = make_uint4(0, 0, 0, 0);
+      if (out_latent && rr < BT)
+        st_stream16(out_latent + ((size_t)rr * H + h) * D + lane * 8, make_uint4(0, 0, 0, 0));
     }
-  }
-  // acc2[nt][i] = C[row 4g + i][dim 32 wave + 16 nt + i16]
+    // ---- weighted sums; a row is complete when the next pair belongs to another row
+    int cur = -1;
+    float acc[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int rr = rr0 + 4 * g + i;
-    if (rr >= BT) continue;
-    const size_t base = ((size_t)rr * H + h) * DV;
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    auto flush = [&]() {
+      const int lr = tile_row(u, cur);
+      const float tq = lane_f32(total, cur * LPR);   // > 0: the row has a pair
+      const float mq = lane_f32(mx, cur * LPR);
+      const float inv = __builtin_amdgcn_rcpf(tq);
+      uint4 wv;
+      wv.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+      wv.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+      wv.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
+      wv.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
+      tile[lr * 64 + (lane ^ (lr & 15))] = wv;
+      // (the row is below BT: it has a pair)
+      if (out_latent) st_stream16(out_latent + ((size_t)row_of(u, cur) * H + h) * D + lane * 8, wv);
+      lse_lane = lane == cur ? mq + __builtin_amdgcn_logf(tq) * kLn2 : lse_lane;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const float sg = 1.f / (1.f + expf(-gv[nt][i]));
-      out[base + 32 * wave + 16 * nt + i16] = bf16_bits(acc2[nt][i] * sg);
+      for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    };
+    auto consume = [&]() {
+#pragma unroll
+      for (int k = 0; k < kEpiPairs; ++k) {
+        if (bits[k] < 0) break;
+        const int qq = bits[k] / LPR;
+        if (qq != cur) {
+          if (cur >= 0) flush();
+          cur = qq;
+        }
+        const float ws = lane_f32(wl, bits[k]);
+        const uint32_t w4[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += ws * bf16_to_f32(w4[e] & 0xFFFFu);
+          acc[2 * e + 1] += ws * bf16_to_f32(w4[e] >> 16);
+        }
+      }
+    };
+    consume();
+    while (m_rest) {   // a unit with more than kEpiPairs pairs
+      issue(u);
+      consume();
+    }
+    if (cur >= 0) flush();
+    if (lane < G && row_of(u, lane) < BT) lse[(size_t)row_of(u, lane) * H + h] = lse_lane;
+
+    // ---- the next unit's pairs and the LSEs of the one after go out now.
+    // Unconditionally: after the last unit they repeat it (unused), which
+    // keeps the loads in flight the same on every pass, so the compiler's
+    // waits name exactly the loads they need.
+    weights(min(u + 1, n_units - 1));
+    issue(min(u + 1, n_units - 1));
+    l_raw = lse_load(u + 2);
+
+    // ---- block complete: out = tile . W_UV[h]^T, gated
+    if (u % NG == NG - 1) {
+      __syncthreads();
+      // (tile rows past BT hold zeros: they are rows without a visible key)
+      f32x4 acc2[4];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) acc2[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) {
+        const bf16x8 bv = __builtin_bit_cast(bf16x8, wreg[ks]);
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          const int r = 16 * rb + i16;
+          acc2[rb] = mfma16(__builtin_bit_cast(bf16x8, tile[r * 64 + ((4 * ks + g) ^ i16)]), bv, acc2[rb]);
+        }
+      }
+      // acc2[rb][i] = out[row 16 rb + 4 g + i of the block][dim 16 wave + i16]
+      const int b = u / NG;
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rr = (blk0 + b) * kEpiRows + 16 * rb + 4 * g + i;
+          if (rr >= BT) continue;
+          const float sg = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-kLog2e * bf16_to_f32(gb[rb][i])));
+          out[((size_t)rr * H + h) * DV + 16 * wave + i16] = bf16_bits(acc2[rb][i] * sg);
+        }
+      load_gates(min(b + 1, n_units / NG - 1));
+      __syncthreads();   // the tile is rewritten by the next block's units
     }
   }
 }
@@ -2020,11 +2087,6 @@ int ensure_device() {
                 hipSuccess;
       fail |= hipFuncSetAttribute(reinterpret_cast<const void*>(absorb_q_kernel<512>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, DV * 512 * 2) != hipSuccess;
-      const void* epi[] = {reinterpret_cast<const void*>(gated_epilogue_kernel<4, true>),
-                           reinterpret_cast<const void*>(gated_epilogue_kernel<2, true>),
-                           reinterpret_cast<const void*>(gated_epilogue_kernel<1, true>)};
-      for (const void* f : epi)
-        fail |= hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kWuvLdsBytes) != hipSuccess;
       // this device's copy of the static scratch (with this device current)
       void* sp = nullptr;
       fail |= hipGetSymbolAddress(&sp, HIP_SYMBOL(scratch)) != hipSuccess || sp == nullptr;
@@ -2193,17 +2255,22 @@ int gated_call(const mla_verify_params* p, const mla::Plan& pl, const mla_bf16* 
   const int rc = run_attention(p, pl, q_latent, latent_kv_pages, block_table, kv_bounds, nullptr, nullptr, true,
                      part_o, part_lse, st, partials_stay_in_l2(p, pl));
   if (rc != MLA_OK) return rc;
-  const unsigned grid = (unsigned)(((bt_rows + 15) / 16) * p->num_heads);
+  // one workgroup per CU when the heads leave room: a head's blocks are
+  // shared among ceil(CUs / H) workgroups (W_UV[h] is loaded once per
+  // workgroup), each taking a run of consecutive blocks
+  const int n_blk = (bt_rows + kEpiRows - 1) / kEpiRows;
+  const int wg_per_head = std::max(1, std::min(n_blk, mla::kNumCUs / p->num_heads));
+  const int blocks_per_wg = (n_blk + wg_per_head - 1) / wg_per_head;
+  const unsigned grid = (unsigned)(((n_blk + blocks_per_wg - 1) / blocks_per_wg) * p->num_heads);
   const int S = pl.splits;
-  // a grid that fits one workgroup per CU stages W_UV[h] in LDS up front
-  const bool wpre = grid <= (unsigned)mla::kNumCUs;
-  auto go = [&](auto kernel, bool wp) {
-    return mla::launch(kernel, dim3(grid), dim3(kThreads), wp ? kWuvLdsBytes : 0, st, part_o, part_lse, w_uv,
-                       gate_logits, out, lse, out_latent, bt_rows, p->num_heads, S);
+  auto go = [&](auto kernel) {
+    return mla::launch(kernel, dim3(grid), dim3(kEpiThreads), 0, st, part_o, part_lse, w_uv, gate_logits, out,
+                       lse, out_latent, bt_rows, p->num_heads, S, blocks_per_wg);
   };
-  if (S <= 8) return wpre ? go(gated_epilogue_kernel<4, true>, true) : go(gated_epilogue_kernel<4, false>, false);
-  if (S <= 16) return wpre ? go(gated_epilogue_kernel<2, true>, true) : go(gated_epilogue_kernel<2, false>, false);
-  return wpre ? go(gated_epilogue_kernel<1, true>, true) : go(gated_epilogue_kernel<1, false>, false);
+  if (S <= 8) return go(gated_epilogue_kernel<8>);
+  if (S <= 16) return go(gated_epilogue_kernel<16>);
+  if (S <= 32) return go(gated_epilogue_kernel<32>);
+  return go(gated_epilogue_kernel<64>);
 }
 
 // Host checks shared by the two gated entry points.
