@@ -233,6 +233,17 @@ __device__ __forceinline__ void mfma16_vacc_aq(f32x4& acc, const bf16x8& a_op, c
   asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
                : "+v"(acc) : "v"(a_op), "a"(b_op));
 }
+// The same three without the leading wait states, for an MFMA none of whose
+// sources a VALU instruction can have written within the two instructions
+// before it: operands straight from LDS reads, loop-invariant registers, and
+// accumulators only MFMAs write.  The first MFMA of a chain after the VALU
+// work that produced its operands keeps the guarded form.
+__device__ __forceinline__ void mfma16_acc_nw(f32x4& acc, const bf16x8& a_op, const bf16x8& b_op) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a_op), "v"(b_op));
+}
+__device__ __forceinline__ void mfma16_vacc_nw(f32x4& acc, const bf16x8& a_op, const bf16x8& b_op) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a_op), "v"(b_op));
+}
 // Wait states between the last MFMAs writing `acc` and a VALU access of it:
 // callers settle the accumulators of the last 8 PV MFMAs in write order, so
 // with the 3 issue slots of every later MFMA each is at least 24 wait states
@@ -1191,8 +1202,13 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const uint16_t* q, const
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) {
       if (ks + KR - 1 < 16) kop[(ks + KR - 1) % KR] = load_k(ks + KR - 1);
-      mfma16_vacc(acc[0][ks & 1], kop[ks % KR], qreg[0][ks]);
-      mfma16_vacc(acc[1][ks & 1], kop[ks % KR], qreg[1][ks]);
+      if (ks < 2) {   // first MFMA of each chain: its accumulator was just zeroed
+        mfma16_vacc(acc[0][ks & 1], kop[ks % KR], qreg[0][ks]);
+        mfma16_vacc(acc[1][ks & 1], kop[ks % KR], qreg[1][ks]);
+      } else {
+        mfma16_vacc_nw(acc[0][ks & 1], kop[ks % KR], qreg[0][ks]);
+        mfma16_vacc_nw(acc[1][ks & 1], kop[ks % KR], qreg[1][ks]);
+      }
       after(ks);
     }
     // MFMA result -> VALU read: at least 11 wait states after the last MFMA
@@ -1254,8 +1270,13 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const uint16_t* q, const
 #pragma unroll
     for (int d = 0; d < ND; ++d) {
       if (d + VR - 1 < ND) vop[(d + VR - 1) % VR] = load_v(d + VR - 1);
-      mfma16_acc(o[d][0], vop[d % VR], __builtin_bit_cast(bf16x8, pcur[0]));
-      mfma16_acc(o[d][1], vop[d % VR], __builtin_bit_cast(bf16x8, pcur[1]));
+      if (d == 0) {   // the P operands were just packed by VALU instructions
+        mfma16_acc(o[d][0], vop[d % VR], __builtin_bit_cast(bf16x8, pcur[0]));
+        mfma16_acc(o[d][1], vop[d % VR], __builtin_bit_cast(bf16x8, pcur[1]));
+      } else {
+        mfma16_acc_nw(o[d][0], vop[d % VR], __builtin_bit_cast(bf16x8, pcur[0]));
+        mfma16_acc_nw(o[d][1], vop[d % VR], __builtin_bit_cast(bf16x8, pcur[1]));
+      }
     }
   };
 
