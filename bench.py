@@ -454,10 +454,12 @@ def measure(cfg, args, steps, warmup, n_samples, lib, timer, with_kv_updates):
     import torch
 
     import speculative_verify_attention_absorbed_amd as mv
-    from verify_inputs import fp8_cache, make_config
+    from verify_inputs import fp8_cache, make_config, ramp_scores
 
     dev = torch.device("cuda:0")
-    x = make_config(cfg, sharp=args.scores == "sharp")
+    x = make_config(cfg, sharp=args.scores in ("sharp", "ramp"))
+    if args.scores == "ramp":
+        x = ramp_scores(x)   # most row tiles then take the softmax's second pass
     fp8 = args.kv == "fp8"
     if fp8:
         x = fp8_cache(x)     # the same draws, stored as E4M3 codes
@@ -595,8 +597,9 @@ def main():
     ap.add_argument("--warm", action="store_true", help="one pool copy (cache-warm)")
     ap.add_argument("--noncausal", action="store_true",
                     help="every token of a group sees the group's largest bound (draft-block fold)")
-    ap.add_argument("--scores", choices=["stated", "sharp"], default="stated",
-                    help="query scale: the stated draws, or the sharp variant (scaled-score spread ~3)")
+    ap.add_argument("--scores", choices=["stated", "sharp", "ramp"], default="stated",
+                    help="query scale: the stated draws, the sharp variant (scaled-score spread ~3), "
+                         "or sharp with scores drifting by ~200 nats along each context")
     ap.add_argument("--kv", choices=["bf16", "fp8"], default="bf16",
                     help="latent cache storage: bf16, or fp8 E4M3 codes with one scale (2^-8)")
     ap.add_argument("--cpu-runs", type=int, default=3)

@@ -1023,7 +1023,7 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const uint16_t* q, const
   constexpr int ND = 32;                  // 16-dim blocks of a row's O
   constexpr int AHEAD = MLA_ROWS_AHEAD;   // units in flight ahead of the one computed
   constexpr int KR = 8;                   // K operands in flight (QK)
-  constexpr int VR = 6;                   // V operands in flight (PV)
+  constexpr int VR = 8;                   // V operands in flight (PV)
   constexpr int SPITCH = 1040;            // staged output row pitch (bytes)
   static_assert(NBUF == 4 && AHEAD < NBUF, "staging ring");
   static_assert(RT * SPITCH <= kBufBytes + kPBytes, "row staging");

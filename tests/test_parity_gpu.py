@@ -14,7 +14,7 @@ from gpu_util import (assert_close_output, assert_lse, assert_masked_rows_zero, 
                       bf16_tensor, f64_of, log, rel_l2, round_bf16, sync, upload,
                       upload_dense_pool)
 from probes import needle_case, needle_expected
-from verify_inputs import build_inputs, make_config
+from verify_inputs import build_inputs, make_config, ramp_scores
 
 pytestmark = pytest.mark.gpu
 
@@ -81,6 +81,28 @@ def test_latent_parity_config5_full():
     q_bits = oracle_qlat_bits(x)
     d = upload(x, q_latent_bits=q_bits)
     check_latent(x, d, q_bits, what="cfg5")
+
+
+@pytest.mark.parametrize("cfg", [2, 5])
+def test_latent_parity_drifting_scores(cfg):
+    """Sharp scores plus a drift of up to ~200 nats along each context
+    (ramp_scores): most row tiles meet a score more than 64 (log2) above
+    their first unit's maximum, so the item runs the softmax's second pass.
+    The drift adds up to ~10 to latent values, so outputs reach that size:
+    the max-abs bar applies to outputs divided by their largest magnitude,
+    the L2 and LSE bars as stated."""
+    log(f"latent parity: config {cfg}, sharp scores drifting along the context")
+    x = ramp_scores(make_config(cfg, sharp=True))
+    q_bits = oracle_qlat_bits(x)
+    d = upload(x, q_latent_bits=q_bits)
+    got, lse, _ = run_latent(x, d)
+    want, want_lse = oracle.verify_attention_latent(q_bits, x.pool, x.block_table, x.kv_bounds,
+                                                    x.sm_scale)
+    assert_lse(lse, want_lse, "drift lse")
+    assert_masked_rows_zero(got, want_lse, "drift out_latent")
+    scale = max(1.0, float(np.abs(want).max()))
+    log(f"  output scale {scale:.2f}")
+    assert_close_output(got / scale, want / scale, "drift out_latent (scaled)")
 
 
 @pytest.mark.parametrize("tile", [32, 64, 128])

@@ -283,6 +283,38 @@ def make_config(n: int, seed: int | None = None, *, sharp: bool = False,
                    permute_single=(spec.ctx == "fixed256"))
 
 
+def ramp_scores(inp: VerifyInputs, rise: float = 200.0, seed: int = 7) -> VerifyInputs:
+    """The same batch with scores that drift along each request's context.
+
+    Key j of a request with n visible keys gets ``(j / n) * r`` times one
+    seeded random unit vector u added to its latent row, with
+    ``r = rise / (sm_scale * sigma)`` and sigma the spread of an absorbed
+    query's projection on u implied by the draws (sqrt(128)/512 times the
+    query scale).  A query whose projection is one sigma above zero then sees
+    its scores rise by ``rise`` nats from the first key to the last; half the
+    queries rise, half fall.  (Stress input for the softmax's reference
+    handling; the drift is in the cache, so every row of a request sees it.)
+    """
+    q_scale = float(np.std(bf16_bits_to_f32(inp.q_nope))) * math.sqrt(LATENT) or 1.0
+    sigma = math.sqrt(NOPE) / LATENT * q_scale
+    r = rise / (inp.sm_scale * sigma)
+    u = np.random.default_rng(seed).standard_normal(LATENT)
+    u /= np.linalg.norm(u)
+    pages = bf16_bits_to_f32(inp.pool.pages).copy()          # [n_pages, 64, 512]
+    slot = inp.pool.slot
+    n_keys = np.clip(inp.kv_bounds.max(axis=1), 0, None)
+    for b in range(inp.block_table.shape[0]):
+        n = int(n_keys[b])
+        if n == 0:
+            continue
+        j = np.arange(n)
+        s = slot[inp.block_table[b, j // PAGE]]
+        pages[s, j % PAGE] += ((j / n) * r)[:, None].astype(np.float32) * u[None, :].astype(np.float32)
+    out = dataclasses.replace(inp)
+    out.pool = SparsePool(inp.pool.num_pages, inp.pool.page_ids, f32_to_bf16_bits(pages))
+    return out
+
+
 def bf16_bits_to_fp8_codes(bits, kv_scale: float) -> np.ndarray:
     """E4M3 codes of bf16 values divided by ``kv_scale``: round to nearest
     even, NaN stays NaN (code 0x7F).  The encoding is torch's float8_e4m3fn
