@@ -104,6 +104,9 @@ enum mla_verify_kv_dtype {
 #define MLA_VERIFY_MAX_Q_LEN 16
 #define MLA_VERIFY_MAX_HEADS 128
 #define MLA_VERIFY_MAX_SPLITS 64
+/* Balanced-chunk partition (mla_verify_attn_partials): the start-up cost of
+ * one (request, chunk) item, counted in 32-key units of key-loop time. */
+#define MLA_VERIFY_ITEM_UNITS 6
 /* Device scratch behind mla_verify_attn_gated_noalloc (64 MiB per GPU). */
 #define MLA_VERIFY_STATIC_SCRATCH_BYTES (64u << 20)
 
@@ -186,13 +189,16 @@ int mla_verify_attn(const mla_verify_params* p,
  * of its rows.
  *  - Tiles of 128 rows on a bf16 cache with S >= 2 and B <= 2000 (balanced
  *    chunks): request b has U_b = ceil(n_b / 32) units of 32 keys, n_b its
- *    largest bound.  The requests' units laid end to end (request b starting
- *    at unit st_b = U_0 + ... + U_(b-1), U units in all) are cut into chunks
- *    of C = max(ceil(U / g), ceil(2 P / (S - 1))) units, g = 8 *
- *    floor(32 / (tiles per request)); the last chunk runs to the end.  Slot
- *    j of request b covers the units of chunk floor(st_b / C) + j that
- *    belong to it, as request keys [32 a, 32 a') (each tile clips them to
- *    its own L); its slots past its last chunk are empty (lse = -inf).
+ *    largest bound, and occupies V_b = U_b + F positions (F =
+ *    MLA_VERIFY_ITEM_UNITS; V_b = 0 when U_b = 0): F for its start-up, then
+ *    its units.  The requests laid end to end (request b at position
+ *    st_b = V_0 + ... + V_(b-1), V positions in all; its units at
+ *    positions st_b + F ...) are cut into chunks of C = max(ceil(V / g),
+ *    ceil(2 P / (S - 1))) positions, g = 8 * floor(32 / (tiles per
+ *    request)); the last chunk runs to the end.  Slot j of request b covers
+ *    the units of chunk floor((st_b + F) / C) + j that belong to it, as
+ *    request keys [32 a, 32 a') (each tile clips them to its own L); its
+ *    slots past its last chunk are empty (lse = -inf).
  *  - Otherwise a tile's n = ceil(L / 64) pages go to S' = min(S, ceil(n / m))
  *    contiguous splits, split s < S' holding pages [floor(s n / S'),
  *    floor((s+1) n / S')), with m = max(1, floor(ceil(P / S) / 2)); splits

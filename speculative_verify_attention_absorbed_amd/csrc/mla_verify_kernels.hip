@@ -1468,8 +1468,12 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const uint16_t* q, const
   //   per-tile splits (!balanced): one item, (request, split, row tile) from
   //     the grid position.
   //   balanced chunks: request b has U_b = ceil(n_b / 32) units (n_b its
-  //     largest bound); the requests' units laid end to end are cut into G
-  //     chunks of C units, C = max(ceil(U / groups), chunk_min).  A group of
+  //     largest bound) and takes MLA_VERIFY_ITEM_UNITS more positions ahead
+  //     of them for an item's start-up (Q, bounds and table, the first
+  //     units' latency, the finalize: about 27k cycles against 4.8k per
+  //     unit), so that a chunk crossing many short requests gets fewer
+  //     units; the requests' positions laid end to end are cut into G
+  //     chunks of C positions, C = max(ceil(V / groups), chunk_min).  A group of
   //     row_tiles workgroups on one XCD (one per row tile, so the tiles of a
   //     request stream the same pages through one L2 together) takes chunk
   //     grp: for every request the chunk touches, its rows over those units,
@@ -1506,7 +1510,8 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const uint16_t* q, const
         int nb = 0;
         if (bq < a.B)
           for (int t = 0; t < a.T; ++t) nb = max(nb, clampi(a.bounds[(size_t)bq * a.T + t], 0, max_keys));
-        cnt[j] = (nb + UK - 1) / UK;
+        const int ub = (nb + UK - 1) / UK;
+        cnt[j] = ub > 0 ? ub + MLA_VERIFY_ITEM_UNITS : 0;   // start-up, then the units
         sum += cnt[j];
       }
       int incl = sum;
@@ -1558,15 +1563,18 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const uint16_t* q, const
     if (a.balanced) {
       const int st = __builtin_amdgcn_readfirstlane(s_start[b]);
       if (st >= hi) break;
-      const int Ub = __builtin_amdgcn_readfirstlane(s_start[b + 1]) - st;
-      if (Ub == 0) {
+      const int Vb = __builtin_amdgcn_readfirstlane(s_start[b + 1]) - st;
+      if (Vb == 0) {
         if (min(st / C, G - 1) == grp) clear_slots(b, 0);
         continue;
       }
-      slot = grp - st / C;
-      ua = max(lo - st, 0);
-      ub = min(hi - st, Ub);
-      if (hi - st >= Ub) tail = slot + 1;   // this group holds the request's last unit
+      const int su = st + MLA_VERIFY_ITEM_UNITS;   // position of the request's first unit
+      const int Ub = Vb - MLA_VERIFY_ITEM_UNITS;
+      if (hi <= su) break;                           // this chunk holds only its start-up share
+      slot = grp - su / C;
+      ua = max(lo - su, 0);
+      ub = min(hi - su, Ub);
+      if (hi - su >= Ub) tail = slot + 1;   // this group holds the request's last unit
     }
     run_item(b, rt, slot, ua, ub, !a.balanced);
     if (tail < a.S) clear_slots(b, tail);

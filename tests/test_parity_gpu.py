@@ -391,19 +391,25 @@ def library_split_count(n_keys, num_splits, max_pages):
     return min(num_splits, max(1, -(-n_pg // m)))
 
 
+ITEM_UNITS = 6   # MLA_VERIFY_ITEM_UNITS
+
+
 def balanced_chunks(x, splits, tile):
     """Key ranges of every partial slot under the balanced-chunk partition the
     header documents for 128-row tiles on a bf16 cache (split count >= 2):
-    request b has U_b = ceil(n_b / 32) units, n_b its largest bound; the
-    requests' units end to end are cut into chunks of C = max(ceil(U / g),
-    ceil(2 P / (S - 1))) units, g = 8 * floor(32 / row tiles); slot j of
-    request b is its part of chunk floor(start_b / C) + j.  Returns
-    {b: [(k0, k1), ...]} in request keys (before each tile's own clip)."""
+    request b has U_b = ceil(n_b / 32) units, n_b its largest bound, and
+    takes V_b = U_b + F positions (0 if U_b = 0), its units after the first
+    F; the requests' positions end to end are cut into chunks of
+    C = max(ceil(V / g), ceil(2 P / (S - 1))), g = 8 * floor(32 / row tiles);
+    slot j of request b is its part of chunk floor((start_b + F) / C) + j.
+    Returns {b: [(k0, k1), ...]} in request keys (before each tile's own
+    clip)."""
     b_n, t, h = x.shape
     max_pages = x.block_table.shape[1]
     n_b = np.clip(x.kv_bounds, 0, max_pages * 64).max(axis=1)
     units = [-(-int(n) // 32) for n in n_b]
-    starts = np.concatenate([[0], np.cumsum(units)]).astype(int)
+    spans = [u + ITEM_UNITS if u > 0 else 0 for u in units]
+    starts = np.concatenate([[0], np.cumsum(spans)]).astype(int)
     total = int(starts[-1])
     row_tiles = -(-(t * h) // tile)
     groups = 8 * (32 // row_tiles)
@@ -411,7 +417,7 @@ def balanced_chunks(x, splits, tile):
     g_used = max(1, -(-total // c))
     out = {}
     for bi in range(b_n):
-        st, ub = int(starts[bi]), units[bi]
+        st, ub = int(starts[bi]) + ITEM_UNITS, units[bi]
         rng = []
         if ub > 0:
             q0, q1 = st // c, (st + ub - 1) // c
