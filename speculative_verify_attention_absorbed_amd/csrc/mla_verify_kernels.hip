@@ -1592,6 +1592,7 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const uint16_t* q, const
 //           hardware's base-2 units (v_exp_f32, v_log_f32, 1 ulp).
 //   S > 16: lane s fetches split s's LSE, the weights are reduced across
 //           lanes, and the partials stream in batches of 16.
+template <int F>   // loads in the first batch: 4 when S <= 4, else 8
 __device__ __forceinline__ float merge_row(const uint16_t* __restrict__ part_o,
                                            const float* __restrict__ part_lse, int S,
                                            size_t stride_rows, size_t row, int lane, float out[8]) {
@@ -1602,10 +1603,15 @@ __device__ __forceinline__ float merge_row(const uint16_t* __restrict__ part_o,
     // split indices clamped to a valid one: the loads are unconditional and
     // issue back to back; a second batch only when there are more than 8
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < F; ++j) {
       const size_t r = (size_t)min(j, sl) * stride_rows + row;
       lj[j] = part_lse[r];
       v[j] = ld_stream16(part_o + r * D + lane * 8);
+    }
+#pragma unroll
+    for (int j = F; j < 8; ++j) {
+      lj[j] = -INFINITY;
+      v[j] = make_uint4(0, 0, 0, 0);
     }
     if (S > 8) {
 #pragma unroll
@@ -1699,6 +1705,7 @@ __device__ __forceinline__ float merge_row(const uint16_t* __restrict__ part_o,
   return mx + logf(total);
 }
 
+template <int F>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const uint16_t* __restrict__ part_o,
                                                            const float* __restrict__ part_lse,
                                                            uint16_t* __restrict__ out_lat,
@@ -1718,7 +1725,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint16_t* __res
   }
   if (row >= rows) return;
   float v[8];
-  const float l = merge_row(part_o, part_lse, S, (size_t)rows, (size_t)row, lane, v);
+  const float l = merge_row<F>(part_o, part_lse, S, (size_t)rows, (size_t)row, lane, v);
   uint4 w;
   w.x = pack_bf16x2(v[0], v[1]);
   w.y = pack_bf16x2(v[2], v[3]);
@@ -2194,6 +2201,16 @@ int run_attention(const mla_verify_params* p, const mla::Plan& pl, const mla_bf1
 
 }  // namespace
 
+// The combine for S splits: a first batch of 4 partial loads per lane when
+// S <= 4 (8 would load each partial twice), else 8.
+int launch_combine(int S, dim3 grid, hipStream_t st, const mla_bf16* part_o, const float* part_lse,
+                   mla_bf16* out_latent, float* lse, int rows, int R, int per) {
+  auto go = [&](auto kernel) {
+    return mla::launch(kernel, grid, dim3(kThreads), 0, st, part_o, part_lse, out_latent, lse, rows, S, R, per);
+  };
+  return S <= 4 ? go(combine_kernel<4>) : go(combine_kernel<8>);
+}
+
 namespace mla {
 int device_ready() { return ensure_device(); }
 }  // namespace mla
@@ -2231,11 +2248,10 @@ int mla_verify_attn(const mla_verify_params* p, const mla_bf16* q_latent,
       const int b_hi = std::min(p->batch, ((x + 1) * per + pl.splits - 1) / pl.splits);
       most = std::max(most, (b_hi - b_lo) * pl.rows);
     }
-    return mla::launch(combine_kernel, dim3(mla::kNumXCDs * ((most + 3) / 4)), dim3(kThreads), 0, st, part_o,
-                       part_lse, out_latent, lse, rows, pl.splits, pl.rows, per);
+    return launch_combine(pl.splits, dim3(mla::kNumXCDs * ((most + 3) / 4)), st, part_o, part_lse, out_latent,
+                          lse, rows, pl.rows, per);
   }
-  return mla::launch(combine_kernel, dim3((rows + 3) / 4), dim3(kThreads), 0, st, part_o, part_lse, out_latent,
-                     lse, rows, pl.splits, 0, 0);
+  return launch_combine(pl.splits, dim3((rows + 3) / 4), st, part_o, part_lse, out_latent, lse, rows, 0, 0);
 }
 
 int mla_verify_attn_partials(const mla_verify_params* p, const mla_bf16* q_latent,
@@ -2261,8 +2277,8 @@ int mla_verify_lse_combine(int num_splits, int rows, const mla_bf16* part_o, con
   if (mla::any_misaligned({part_o, part_lse, out_latent, lse})) return MLA_ERR_ARG;
   const int rc = ensure_device();
   if (rc != MLA_OK) return rc;
-  return mla::launch(combine_kernel, dim3((rows + 3) / 4), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
-                     part_o, part_lse, out_latent, lse, rows, num_splits, 0, 0);
+  return launch_combine(num_splits, dim3((rows + 3) / 4), static_cast<hipStream_t>(stream), part_o, part_lse,
+                        out_latent, lse, rows, 0, 0);
 }
 
 }  // extern "C"
