@@ -1140,10 +1140,14 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const uint16_t* q, const
     uint32_t buf;           // LDS byte offset of the unit's buffer
     int valid;              // rows of the unit to fetch
   };
-  auto stage_of = [&](int u) {
+  // The page id of unit u as read from LDS (clamped to the range's last
+  // unit); the loop reads it one iteration before it stages the unit, so the
+  // LDS round trip is not on the staging's path.
+  auto pid_of = [&](int u) { return sm_pid[(k_begin + min(u, max(n_units - 1, 0)) * UK) / PG - pid_base]; };
+  auto stage_of = [&](int u, int pid_raw) {
     Stage st;
     const int key0 = k_begin + u * UK;   // the unit's first key (a multiple of 32)
-    const int pid = __builtin_amdgcn_readfirstlane(sm_pid[key0 / PG - pid_base]);
+    const int pid = __builtin_amdgcn_readfirstlane(pid_raw);
     const bool pid_ok = (unsigned)pid < (unsigned)a.N;
     st.valid = pid_ok ? n_tile - key0 : 0;
     st.base = reinterpret_cast<const uint16_t*>(a.pool) + ((size_t)(pid_ok ? pid : 0) * PG + (key0 & 63)) * D;
@@ -1302,11 +1306,11 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const uint16_t* q, const
     uint32_t ops_ring = 0;   // DMA count of unit v at bits 8 (v % NBUF)
     auto ring_set = [&](int v, int ops) {
       const uint32_t sh = 8u * (uint32_t)(v % NBUF);
-      ops_ring = (ops_ring & ~(0xFFu << sh)) | ((uint32_t)ops << sh);
+      ops_ring = __builtin_amdgcn_readfirstlane((ops_ring & ~(0xFFu << sh)) | ((uint32_t)ops << sh));
     };
     auto ring_get = [&](int v) { return (int)((ops_ring >> (8 * (v % NBUF))) & 0xFFu); };
-    auto stage_unit = [&](int v) {
-      const Stage st = stage_of(v);
+    auto stage_unit = [&](int v, int pid_raw) {
+      const Stage st = stage_of(v, pid_raw);
       if (st.valid >= UK) {   // a whole unit: one DMA per row, no per-row test
 #pragma unroll
         for (int i = 0; i < ROWS_PW; ++i) stage_row(st, i, true);
@@ -1330,18 +1334,26 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const uint16_t* q, const
     // unit 0, unconditionally: the compiler does not count the staging DMAs,
     // so any wait it placed for Q inside the key loop would also wait for
     // the units in flight.
-    if (n_units > 0) stage_unit(0);
+    if (n_units > 0) stage_unit(0, pid_of(0));
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-    for (int v = 1; v < AHEAD && v < n_units; ++v) stage_unit(v);
+    for (int v = 1; v < AHEAD && v < n_units; ++v) stage_unit(v, pid_of(v));
+    int pid_next = pid_of(AHEAD);
     for (int u = 0; u < n_units; ++u) {
       int newer = 0;   // DMA instructions issued after unit u's
 #pragma unroll
       for (int j = 1; j < AHEAD; ++j) newer += (u + j < n_units) ? ring_get(u + j) : 0;
-      wait_vm_barrier(__builtin_amdgcn_readfirstlane(newer));   // unit u staged; iteration u-1 done everywhere
+      // unit u staged; iteration u-1 done everywhere (whole units in flight
+      // behind it: the common case, without the general wait's branches)
+      newer = __builtin_amdgcn_readfirstlane(newer);
+      if (newer == (AHEAD - 1) * ROWS_PW)
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((AHEAD - 1) * ROWS_PW) : "memory");
+      else
+        wait_vm_barrier(newer);
       // the unit AHEAD past u, into the buffer unit u-1 released (one burst:
       // each DMA issue stalls the wave while the memory pipeline is busy, and
       // spread between the MFMAs those stalls cost more)
-      if (u + AHEAD < n_units) stage_unit(u + AHEAD);
+      if (u + AHEAD < n_units) stage_unit(u + AHEAD, pid_next);
+      pid_next = pid_of(u + AHEAD + 1);
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         mt[rb] = mtrue[rb];
