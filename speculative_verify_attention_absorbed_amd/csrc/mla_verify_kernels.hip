@@ -244,6 +244,11 @@ __device__ __forceinline__ void mfma16_acc_nw(f32x4& acc, const bf16x8& a_op, co
 __device__ __forceinline__ void mfma16_vacc_nw(f32x4& acc, const bf16x8& a_op, const bf16x8& b_op) {
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a_op), "v"(b_op));
 }
+// The first MFMA of a chain: the accumulator input is the inline constant 0,
+// so the accumulator needs no clearing (and no VALU write precedes it).
+__device__ __forceinline__ void mfma16_vzero_nw(f32x4& acc, const bf16x8& a_op, const bf16x8& b_op) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a_op), "v"(b_op));
+}
 // Wait states between the last MFMAs writing `acc` and a VALU access of it:
 // callers settle the accumulators of the last 8 PV MFMAs in write order, so
 // with the 3 issue slots of every later MFMA each is at least 24 wait states
@@ -986,6 +991,9 @@ __global__ __launch_bounds__(256) void attn_kernel(const uint16_t* q, const int3
 #ifndef MLA_ROWS_AHEAD
 #define MLA_ROWS_AHEAD 3
 #endif
+#ifndef MLA_QK_CHAINS
+#define MLA_QK_CHAINS 1
+#endif
 // Verify attention over one (request b, KV split s, 128-row tile) work item,
 // bf16 cache, with every wave owning 32 folded rows for the whole
 // computation (wave w: tile rows 32 w .. +31):
@@ -1042,7 +1050,6 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const uint16_t* q, const
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 4, i16 = lane & 15;
 
   const int max_keys = a.P * PG;
 
@@ -1194,11 +1201,10 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const uint16_t* q, const
   // after the MFMAs of k-step ks (VALU work that overlaps them).
   auto qk_half = [&](int u, int kb, f32x4 (&s)[2], auto&& after) {
     const uint32_t kbase = (uint32_t)(u % NBUF) * UB + 16384u * (uint32_t)kb;
-    // even and odd k-steps accumulate apart: four independent MFMA chains,
-    // so no MFMA waits for the result of the one before it
-    f32x4 acc[2][2];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) acc[rb][0] = acc[rb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // MLA_QK_CHAINS accumulator chains per row block (k-step ks feeds chain
+    // ks % chains); each chain starts from a zero accumulator input
+    constexpr int CH = MLA_QK_CHAINS;
+    f32x4 acc[2][CH];
     bf16x8 kop[KR];
     auto load_k = [&](int ks) { return *(const lds_bf16x8*)(sb + kbase + qkb[ks & 3] + 256 * (ks >> 2)); };
 #pragma unroll
@@ -1206,19 +1212,25 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const uint16_t* q, const
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) {
       if (ks + KR - 1 < 16) kop[(ks + KR - 1) % KR] = load_k(ks + KR - 1);
-      if (ks < 2) {   // first MFMA of each chain: its accumulator was just zeroed
-        mfma16_vacc(acc[0][ks & 1], kop[ks % KR], qreg[0][ks]);
-        mfma16_vacc(acc[1][ks & 1], kop[ks % KR], qreg[1][ks]);
+      if (ks < CH) {
+        mfma16_vzero_nw(acc[0][ks % CH], kop[ks % KR], qreg[0][ks]);
+        mfma16_vzero_nw(acc[1][ks % CH], kop[ks % KR], qreg[1][ks]);
       } else {
-        mfma16_vacc_nw(acc[0][ks & 1], kop[ks % KR], qreg[0][ks]);
-        mfma16_vacc_nw(acc[1][ks & 1], kop[ks % KR], qreg[1][ks]);
+        mfma16_vacc_nw(acc[0][ks % CH], kop[ks % KR], qreg[0][ks]);
+        mfma16_vacc_nw(acc[1][ks % CH], kop[ks % KR], qreg[1][ks]);
       }
       after(ks);
     }
     // MFMA result -> VALU read: at least 11 wait states after the last MFMA
-    asm volatile("s_nop 7\n\ts_nop 4" : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[1][0]), "+v"(acc[1][1]));
-    s[0] = acc[0][0] + acc[0][1];
-    s[1] = acc[1][0] + acc[1][1];
+    if constexpr (CH == 1) {
+      asm volatile("s_nop 7\n\ts_nop 4" : "+v"(acc[0][0]), "+v"(acc[1][0]));
+      s[0] = acc[0][0];
+      s[1] = acc[1][0];
+    } else {
+      asm volatile("s_nop 7\n\ts_nop 4" : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[1][0]), "+v"(acc[1][1]));
+      s[0] = acc[0][0] + acc[0][1];
+      s[1] = acc[1][0] + acc[1][1];
+    }
   };
 
   // Raw scores of a key half with the keys a row does not see at -inf (a
@@ -1259,8 +1271,13 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const uint16_t* q, const
     }
   };
 
-  // O^T += V^T P^T of unit u over all 512 dims of the wave's 32 rows.
-  auto pv = [&](int u) {
+  // O^T += V^T P^T of unit u over all 512 dims of the wave's 32 rows.  The
+  // second row block's P is still being formed when PV starts: mid(j), the
+  // VALU work that finishes it, rides the first row block's MFMAs of dim
+  // blocks 0..7 (the V operands of those eight stay in registers for the
+  // second row block), then the ring of VR operands runs as usual.
+  static_assert(VR == 8, "the first eight V operands fill the ring");
+  auto pv = [&](int u, auto&& mid) {
     const uint32_t ub = (uint32_t)(u % NBUF) * UB;
     auto load_v = [&](int d) {
       const uint32_t o0 = ub + vrow + 256u * (uint32_t)(d >> 3) + 32u * (uint32_t)((d & 7) ^ vtsw);
@@ -1270,17 +1287,30 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const uint16_t* q, const
     };
     bf16x8 vop[VR];
 #pragma unroll
-    for (int d = 0; d < VR - 1; ++d) vop[d] = load_v(d);
+    for (int d = 0; d < VR; ++d) vop[d] = load_v(d);
 #pragma unroll
-    for (int d = 0; d < ND; ++d) {
+    for (int d = 0; d < VR; ++d) {
+      if (d == 0)   // P of row block 0 was just packed by VALU instructions
+        mfma16_acc(o[d][0], vop[d], __builtin_bit_cast(bf16x8, pcur[0]));
+      else
+        mfma16_acc_nw(o[d][0], vop[d], __builtin_bit_cast(bf16x8, pcur[0]));
+      mid(d);
+      __builtin_amdgcn_sched_barrier(0);   // keep mid(d) between these MFMAs
+    }
+#pragma unroll
+    for (int d = 0; d < VR; ++d) {
+      if (d == 0)   // P of row block 1 was just packed by mid()
+        mfma16_acc(o[d][1], vop[d], __builtin_bit_cast(bf16x8, pcur[1]));
+      else
+        mfma16_acc_nw(o[d][1], vop[d], __builtin_bit_cast(bf16x8, pcur[1]));
+      if (d >= 1) vop[d - 1] = load_v(d - 1 + VR);   // both row blocks are done with dim block d-1
+    }
+    // slots 0..VR-2 hold dim blocks VR..2VR-2, slot VR-1 is free
+#pragma unroll
+    for (int d = VR; d < ND; ++d) {
       if (d + VR - 1 < ND) vop[(d + VR - 1) % VR] = load_v(d + VR - 1);
-      if (d == 0) {   // the P operands were just packed by VALU instructions
-        mfma16_acc(o[d][0], vop[d % VR], __builtin_bit_cast(bf16x8, pcur[0]));
-        mfma16_acc(o[d][1], vop[d % VR], __builtin_bit_cast(bf16x8, pcur[1]));
-      } else {
-        mfma16_acc_nw(o[d][0], vop[d % VR], __builtin_bit_cast(bf16x8, pcur[0]));
-        mfma16_acc_nw(o[d][1], vop[d % VR], __builtin_bit_cast(bf16x8, pcur[1]));
-      }
+      mfma16_acc_nw(o[d][0], vop[d % VR], __builtin_bit_cast(bf16x8, pcur[0]));
+      mfma16_acc_nw(o[d][1], vop[d % VR], __builtin_bit_cast(bf16x8, pcur[1]));
     }
   };
 
@@ -1391,7 +1421,8 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const uint16_t* q, const
         masked(u, 1, s1, sv1);
       }
 #pragma unroll
-      for (int k = 0; k < 16; ++k) sm_step(1, sv1, k);
+      for (int k = 0; k < 8; ++k) sm_step(1, sv1, k);   // row block 0
+      pv(u, [&](int j) { sm_step(1, sv1, 8 + j); });   // row block 1 rides PV's first MFMAs
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         mtrue[rb] = mt[rb];
@@ -1399,7 +1430,6 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const uint16_t* q, const
         lround[rb] = sr[rb];
         lexact[rb] += se[rb];
       }
-      pv(u);
     }
     // MFMA write -> VALU write of the same accumulator (a second pass clears
     // the tile): 24 wait states.  The clear sits behind the branch below.
