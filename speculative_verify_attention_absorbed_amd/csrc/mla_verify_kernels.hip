@@ -1199,19 +1199,26 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const uint16_t* q, const
   // S^T = K Q^T of unit u for the keys 16 kb .. 16 kb + 15:
   // s[rb][i] = score(key 16 kb + 4 g + i, row wrow(rb)).  after(ks) runs
   // after the MFMAs of k-step ks (VALU work that overlaps them).
-  auto qk_half = [&](int u, int kb, f32x4 (&s)[2], auto&& after) {
+  // The K operands travel in a ring of KR registers; the first KR-1 of a
+  // half are loaded by k_prime() (for the first half, ahead of the unit's
+  // DMA burst, so that their LDS latency passes during it).
+  bf16x8 kop[KR];
+  auto load_k = [&](int u, int kb, int ks) {
     const uint32_t kbase = (uint32_t)(u % NBUF) * UB + 16384u * (uint32_t)kb;
+    return *(const lds_bf16x8*)(sb + kbase + qkb[ks & 3] + 256 * (ks >> 2));
+  };
+  auto k_prime = [&](int u, int kb) {
+#pragma unroll
+    for (int ks = 0; ks < KR - 1; ++ks) kop[ks] = load_k(u, kb, ks);
+  };
+  auto qk_half = [&](int u, int kb, f32x4 (&s)[2], auto&& after) {
     // MLA_QK_CHAINS accumulator chains per row block (k-step ks feeds chain
     // ks % chains); each chain starts from a zero accumulator input
     constexpr int CH = MLA_QK_CHAINS;
     f32x4 acc[2][CH];
-    bf16x8 kop[KR];
-    auto load_k = [&](int ks) { return *(const lds_bf16x8*)(sb + kbase + qkb[ks & 3] + 256 * (ks >> 2)); };
-#pragma unroll
-    for (int ks = 0; ks < KR - 1; ++ks) kop[ks] = load_k(ks);
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) {
-      if (ks + KR - 1 < 16) kop[(ks + KR - 1) % KR] = load_k(ks + KR - 1);
+      if (ks + KR - 1 < 16) kop[(ks + KR - 1) % KR] = load_k(u, kb, ks + KR - 1);
       if (ks < CH) {
         mfma16_vzero_nw(acc[0][ks % CH], kop[ks % KR], qreg[0][ks]);
         mfma16_vzero_nw(acc[1][ks % CH], kop[ks % KR], qreg[1][ks]);
@@ -1382,6 +1389,7 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const uint16_t* q, const
       // the unit AHEAD past u, into the buffer unit u-1 released (one burst:
       // each DMA issue stalls the wave while the memory pipeline is busy, and
       // spread between the MFMAs those stalls cost more)
+      k_prime(u, 0);
       if (u + AHEAD < n_units) stage_unit(u + AHEAD, pid_next);
       pid_next = pid_of(u + AHEAD + 1);
 #pragma unroll
@@ -1399,6 +1407,7 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const uint16_t* q, const
       if (first) {
         // every row's reference for the whole item (log2 domain): the maximum
         // over the split's first unit, or the preset of a second pass
+        k_prime(u, 1);
         qk_half(u, 1, s1, [](int) {});
         masked(u, 1, s1, sv1);
 #pragma unroll
@@ -1417,6 +1426,7 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const uint16_t* q, const
       } else {
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) mu[rb] = (mref[rb] == -INFINITY) ? 0.f : mref[rb];
+        k_prime(u, 1);
         qk_half(u, 1, s1, [&](int ks) { sm_step(0, sv0, ks); });
         masked(u, 1, s1, sv1);
       }
