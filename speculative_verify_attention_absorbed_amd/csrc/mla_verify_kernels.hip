@@ -500,10 +500,14 @@ __global__ __launch_bounds__(256) void attn_kernel(const uint16_t* q, const int3
   // fp8: one DMA moves a pair of 512-byte key rows (2 pr, 2 pr + 1), lanes
   // 0-31 the first; a pair that straddles the tile's extent fetches its first
   // row with lanes 0-31 alone and zero-fills the second.
-  auto issue_unit = [&](int u) {
+  // The page id of unit u as read from LDS (clamped to the split's last
+  // unit); the pipeline reads it before the unit's turn to stage, so the LDS
+  // round trip is not on the staging's path.
+  auto pid_of = [&](int u) { return sm_pid[pid0 + ((min(u, max(n_units - 1, 0)) * UK) >> 6)]; };
+  auto issue_unit = [&](int u, int pid_raw) {
     const uint32_t ub = (uint32_t)(u % NBUF) * UB;
     const int kl = u * UK;                         // key offset within the split
-    const int pid = __builtin_amdgcn_readfirstlane(sm_pid[pid0 + (kl >> 6)]);
+    const int pid = __builtin_amdgcn_readfirstlane(pid_raw);
     const bool pid_ok = (unsigned)pid < (unsigned)a.N;
     const int valid = pid_ok ? n_tile - (k_begin + kl) : 0;   // rows of the unit to fetch
     if constexpr (KV8) {
@@ -814,11 +818,13 @@ __global__ __launch_bounds__(256) void attn_kernel(const uint16_t* q, const int3
     uint32_t ops_ring = 0;
     auto ring_get = [&](int v) { return (int)((ops_ring >> (8 * (v % NBUF))) & 0xFFu); };
     int issued = 0;       // units issued so far (uniform)
+    int pid_next = pid_of(0);   // page id of unit `issued`
     auto issue_next = [&]() {
-      const int ops = issue_unit(issued);
+      const int ops = issue_unit(issued, pid_next);
       const uint32_t sh = 8u * (uint32_t)(issued % NBUF);
-      ops_ring = (ops_ring & ~(0xFFu << sh)) | ((uint32_t)ops << sh);
+      ops_ring = __builtin_amdgcn_readfirstlane((ops_ring & ~(0xFFu << sh)) | ((uint32_t)ops << sh));
       ++issued;
+      pid_next = pid_of(issued);
     };
     // Key-split tiles move the staged Q to the registers while unit 0 is in
     // flight.
@@ -872,7 +878,14 @@ __global__ __launch_bounds__(256) void attn_kernel(const uint16_t* q, const int3
       int newer = 0;   // DMA ops issued after unit u's
 #pragma unroll
       for (int j = 1; j <= AHEAD; ++j) newer += (u + j < issued) ? ring_get(u + j) : 0;
-      wait_vm_barrier(__builtin_amdgcn_readfirstlane(newer));   // unit u staged; unit u-1 no longer read
+      // unit u staged; unit u-1 no longer read (AHEAD whole units in flight
+      // behind it: the common case, without the general wait's branches)
+      newer = __builtin_amdgcn_readfirstlane(newer);
+      constexpr int kFullOps = AHEAD * (KV8 ? PAIRS_PW : ROWS_PW);
+      if (newer == kFullOps)
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kFullOps) : "memory");
+      else
+        wait_vm_barrier(newer);
       // unit u-1's buffer is free: the unit AHEAD past u goes there; while
       // the pipeline is still filling, one more joins it
       if (issued < n_units && issued <= u + AHEAD) issue_next();

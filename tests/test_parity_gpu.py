@@ -226,6 +226,9 @@ def test_random_bounds_zero_rows_and_empty_requests():
         check_latent(x, d, x.q_latent, num_splits=s, what=f"S{s}")
     for tile in (32, 128):
         check_latent(x, d, x.q_latent, num_splits=2, tile_rows=tile, what=f"S2 tile{tile}")
+    # the 128-row kernel writing the outputs itself (one split), the all-zero
+    # request included (an item with no unit to stage)
+    check_latent(x, d, x.q_latent, num_splits=1, tile_rows=128, what="S1 tile128")
     # bounds beyond max_pages*64 are clamped to it
     big = bounds.copy()
     big[3, 0] = 10_000_000
