@@ -249,6 +249,13 @@ __device__ __forceinline__ void mfma16_vacc_nw(f32x4& acc, const bf16x8& a_op, c
 __device__ __forceinline__ void mfma16_vzero_nw(f32x4& acc, const bf16x8& a_op, const bf16x8& b_op) {
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a_op), "v"(b_op));
 }
+// The same two with the B operand in accumulation registers.
+__device__ __forceinline__ void mfma16_vacc_aq_nw(f32x4& acc, const bf16x8& a_op, const bf16x8& b_op) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a_op), "a"(b_op));
+}
+__device__ __forceinline__ void mfma16_vzero_aq_nw(f32x4& acc, const bf16x8& a_op, const bf16x8& b_op) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a_op), "a"(b_op));
+}
 // Wait states between the last MFMAs writing `acc` and a VALU access of it:
 // callers settle the accumulators of the last 8 PV MFMAs in write order, so
 // with the 3 issue slots of every later MFMA each is at least 24 wait states
@@ -626,11 +633,17 @@ __global__ __launch_bounds__(256) void attn_kernel(const uint16_t* q, const int3
     const uint32_t ub = (uint32_t)(u % NBUF) * UB;
     const int ukey0 = k_begin + u * UK;            // request position of the unit's first key
     // ---- S^T = K Q^T: sacc[kb][rb][i] = score(key qkey(kb) + 4g + i, row qrow(rb))
+    // bf16: every chain starts from the MFMA's constant-0 accumulator input
+    // and no source of a QK or PV MFMA is written by a VALU instruction (K,
+    // V and P come from LDS, Q from LDS or memory), so they carry no wait
+    // states; fp8 operands are converted by VALU instructions just before
     f32x4 sacc[QKB][QRB];
+    if constexpr (KV8) {
 #pragma unroll
-    for (int kb = 0; kb < QKB; ++kb)
+      for (int kb = 0; kb < QKB; ++kb)
 #pragma unroll
-      for (int rb = 0; rb < QRB; ++rb) sacc[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int rb = 0; rb < QRB; ++rb) sacc[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     constexpr int KPG = 2;   // k-steps per operand group
     bf16x8 kop[2][KPG][QKB];
     auto load_k = [&](bf16x8 (&dst)[KPG][QKB], int grp) {
@@ -665,8 +678,16 @@ __global__ __launch_bounds__(256) void attn_kernel(const uint16_t* q, const int3
         for (int kb = 0; kb < QKB; ++kb)
 #pragma unroll
           for (int rb = 0; rb < QRB; ++rb) {
-            if (rb < 2) mfma16_vacc(sacc[kb][rb], kop[grp & 1][e][kb], qreg[rb][ks]);
-            else mfma16_vacc_aq(sacc[kb][rb], kop[grp & 1][e][kb], qreg[rb][ks]);
+            if constexpr (KV8) {
+              if (rb < 2) mfma16_vacc(sacc[kb][rb], kop[grp & 1][e][kb], qreg[rb][ks]);
+              else mfma16_vacc_aq(sacc[kb][rb], kop[grp & 1][e][kb], qreg[rb][ks]);
+            } else if (ks == 0) {
+              if (rb < 2) mfma16_vzero_nw(sacc[kb][rb], kop[grp & 1][e][kb], qreg[rb][ks]);
+              else mfma16_vzero_aq_nw(sacc[kb][rb], kop[grp & 1][e][kb], qreg[rb][ks]);
+            } else {
+              if (rb < 2) mfma16_vacc_nw(sacc[kb][rb], kop[grp & 1][e][kb], qreg[rb][ks]);
+              else mfma16_vacc_aq_nw(sacc[kb][rb], kop[grp & 1][e][kb], qreg[rb][ks]);
+            }
           }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -788,7 +809,10 @@ __global__ __launch_bounds__(256) void attn_kernel(const uint16_t* q, const int3
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) mfma16_acc(o[dt][rb], vop[dt & 1][kk], pop[rb][kk]);
+        for (int kk = 0; kk < KK; ++kk) {
+          if constexpr (KV8) mfma16_acc(o[dt][rb], vop[dt & 1][kk], pop[rb][kk]);
+          else mfma16_acc_nw(o[dt][rb], vop[dt & 1][kk], pop[rb][kk]);
+        }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
