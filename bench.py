@@ -19,7 +19,9 @@ captured into hipGraphs and replayed (--eager times plain launches).
 
 Timing:
   ms_per_step / value   exactly --steps whole calls between two HIP events
-                        on the stream (after --warmup calls): the mean;
+                        on the stream (after --warmup calls, and more
+                        warm-up replays up to 0.3 s of wall time so the
+                        GPU has left its idle clock): the mean;
   timing.*              --samples calls timed one by one (a HIP event pair
                         around each eagerly launched call, all queued behind
                         a sleep kernel so the host never starves the GPU):
@@ -73,6 +75,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
 RIDGE_FLOP_PER_BYTE = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 MALL_BYTES = 256 << 20
 COPY_PROBE_BYTES = 1 << 30
+WARM_FLOOR_S = 0.3             # least wall time of warm-up replays before a timed region
 HEADLINE_CONFIG = 5
 CSRC = os.path.join(ROOT, "speculative_verify_attention_absorbed_amd", "csrc")
 # what decides the kernels that run and their launch shapes
@@ -352,6 +355,15 @@ class Timer:
             if g_rem is not None:
                 g_rem.replay()
         torch.cuda.synchronize()
+        # then more replays until WARM_FLOOR_S of wall time has passed: a GPU
+        # fresh from idle runs its first milliseconds at a lower clock, which a
+        # few warm-up calls do not cover (20 timed steps after 5 warm-up calls
+        # read 15 % slower than the same calls a second later)
+        t_end = time.perf_counter() + WARM_FLOOR_S
+        while time.perf_counter() < t_end:
+            for _ in range(4):
+                (g if g is not None else g_rem).replay()
+            torch.cuda.synchronize()
         start.record(self.stream)
         for _ in range(n_rep):
             g.replay()
