@@ -57,11 +57,11 @@ TileShape choose_shape(int rows, int batch, int forced_splits) {
       return (int64_t)batch * forced_splits * 2 <= kNumCUs ? TileShape{0} : TileShape{1};
     return rows > 48 && (int64_t)kNumCUs / ((int64_t)batch * 2) >= 4 ? TileShape{0} : TileShape{1};
   }
-  return TileShape{2};
+  return TileShape{3};
 }
 
 TileShape shape_for_rows(int tile_rows) {
-  return TileShape{tile_rows == 32 ? 0 : (tile_rows == 64 ? 1 : 2)};
+  return TileShape{tile_rows == 32 ? 0 : (tile_rows == 64 ? 1 : 3)};
 }
 
 Plan make_plan(const mla_verify_params* p, bool gated) {
@@ -69,8 +69,6 @@ Plan make_plan(const mla_verify_params* p, bool gated) {
   pl.rows = p->q_len * p->num_heads;
   pl.shape = p->tile_rows != 0 ? shape_for_rows(p->tile_rows)
                                : choose_shape(pl.rows, p->batch, p->num_splits);
-  // 128-row tiles on a bf16 cache: the kernel whose waves own their rows
-  if (pl.shape.mode == 2 && p->kv_dtype == MLA_KV_BF16) pl.shape.mode = 3;
   pl.row_tiles = (pl.rows + pl.shape.tile_rows() - 1) / pl.shape.tile_rows();
   int s = p->num_splits;
   if (s == 0) {
@@ -99,7 +97,7 @@ Plan make_plan(const mla_verify_params* p, bool gated) {
   const int per_split = (p->max_pages_per_req + s - 1) / s;
   pl.min_split_pages = per_split / 2 > 1 ? per_split / 2 : 1;
   pl.use_partials = gated || s > 1;
-  // 128-row bf16 tiles with a split count: balanced chunks.  A request of at
+  // 128-row tiles with a split count: balanced chunks.  A request of at
   // most 2 P units spans at most floor((2P - 1) / C) + 2 chunks, which is <= S
   // once C >= ceil(2P / (S - 1)).
   pl.balanced = pl.shape.mode == 3 && s >= 2 && p->batch <= kMaxBalancedBatch;

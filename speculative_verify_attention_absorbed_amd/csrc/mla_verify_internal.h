@@ -19,10 +19,9 @@ constexpr int kMaxBalancedBatch = 2000;   // requests whose unit prefix sums fit
 // Shape of one attention workgroup (always four wavefronts).
 //   mode 0: 32-row tile, 64-key staging units, QK split by keys
 //   mode 1: 64-row tile, 64-key staging units, QK split by keys
-//   mode 2: 128-row tile, 32-key staging units, QK split by rows (fp8 cache)
-// In modes 0-2 PV splits the 512 latent dims between the four waves.
-//   mode 3: 128-row tile, 32-key staging units, bf16 cache: each wave owns
-//           32 rows for QK, softmax and PV alike
+// In modes 0 and 1 PV splits the 512 latent dims between the four waves.
+//   mode 3: 128-row tile, 32-key staging units (attn_rows_kernel, bf16 or fp8
+//           cache): each wave owns 32 rows for QK, softmax and PV alike
 struct TileShape {
   int mode;
   int tile_rows() const { return mode == 0 ? 32 : (mode == 1 ? 64 : 128); }

@@ -9,12 +9,12 @@
 //
 // Kernels:
 //   attn_kernel<MODE, KV8>  one workgroup (4 waves) per (request, row tile,
-//                        KV split); tiles of 32, 64 or 128 folded rows; a bf16
+//                        KV split); tiles of 32 or 64 folded rows; a bf16
 //                        or (KV8) an fp8 E4M3 latent cache, whose codes are
 //                        converted exactly to bf16 for the MFMAs.  The
 //                        split's pages stream HBM -> LDS by LDS-DMA
-//                        (XOR-swizzled 16-byte chunks) in 64- or 32-key units,
-//                        the next ones in flight while one is computed.
+//                        (XOR-swizzled 16-byte chunks) in 64-key units, the
+//                        next ones in flight while one is computed.
 //                        S^T = K Q^T on bf16 MFMA 16x16x32 with Q^T held in
 //                        registers; each row masked by its own bound; softmax
 //                        against a per-row reference max fixed on the split's
@@ -24,6 +24,10 @@
 //                        registers.  Writes bf16 o_lat + lse directly (one
 //                        split), or normalised bf16 partials + fp32 partial
 //                        lse (split-KV).
+//   attn_rows_kernel<KV8>  the same for 128-row tiles, every wave owning 32
+//                        rows for QK, softmax and PV (P stays in registers);
+//                        32-key units; balanced chunks of units per workgroup
+//                        when the tiles are split.
 //   combine_kernel       LSE merge of the S partials of every row (rows with
 //                        no visible key in any split give (-inf, 0)); after
 //                        the contiguous layout with small partials, each
@@ -249,6 +253,11 @@ __device__ __forceinline__ void mfma16_vacc_nw(f32x4& acc, const bf16x8& a_op, c
 __device__ __forceinline__ void mfma16_vzero_nw(f32x4& acc, const bf16x8& a_op, const bf16x8& b_op) {
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a_op), "v"(b_op));
 }
+// The guarded form of mfma16_vzero_nw, for an A operand a VALU instruction
+// just wrote (an fp8 key converted to bf16).
+__device__ __forceinline__ void mfma16_vzero(f32x4& acc, const bf16x8& a_op, const bf16x8& b_op) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a_op), "v"(b_op));
+}
 // The same two with the B operand in accumulation registers.
 __device__ __forceinline__ void mfma16_vacc_aq_nw(f32x4& acc, const bf16x8& a_op, const bf16x8& b_op) {
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a_op), "a"(b_op));
@@ -304,15 +313,14 @@ __device__ __forceinline__ int logical_item(int bid, int n_groups, int row_tiles
   return g < n_groups ? g * row_tiles + pos % row_tiles : -1;
 }
 
-// Verify attention over one (request b, KV split s, row tile) work item.
-// Four wavefronts; MODE picks the tile:
+// Verify attention over one (request b, KV split s, row tile) work item of a
+// 32- or 64-row tile (128-row tiles run attn_rows_kernel).  Four wavefronts;
+// MODE picks the tile:
 //   MODE 0 / 1   a tile of 32 / 64 folded rows (every row of a request with
 //                R <= 64), 64-key staging units.  QK splits the unit's keys
 //                between the waves (wave w: keys 16w .. +15, all rows), so
 //                every latent byte is read from LDS once by the QK reads.
-//   MODE 2       a tile of 128 rows, 32-key units.  QK splits the rows (wave
-//                w: rows 32w .. +31, all 32 keys).
-// In both, PV splits the latent dims (wave w: dims 128w .. +127, all rows):
+// PV splits the latent dims (wave w: dims 128w .. +127, all rows):
 //   S = Q K^T   bf16 MFMA 16x16x32, K from LDS (ds_read_b128), Q^T in
 //               registers for the whole item; masked by each row's own
 //               bound; P = 2^(s - ref) in bf16 goes to a small LDS tile
@@ -341,21 +349,21 @@ __global__ __launch_bounds__(256) void attn_kernel(const uint16_t* q, const int3
   a.H = H;
   a.R = R;
   a.P = P;
-  constexpr bool KS = MODE < 2;                 // key-split QK
-  constexpr int NRB = MODE == 0 ? 2 : (MODE == 1 ? 4 : 8);   // 16-row blocks of the tile
+  static_assert(MODE == 0 || MODE == 1, "32- and 64-row tiles");
+  constexpr int NRB = MODE == 0 ? 2 : 4;        // 16-row blocks of the tile
   constexpr int RT = 16 * NRB;                  // rows per tile
-  constexpr int UK = KS ? 64 : 32;              // keys per staging unit
+  constexpr int UK = 64;                        // keys per staging unit
   constexpr int ROWB = KV8 ? 512 : 1024;        // LDS bytes per staged key row
   constexpr int UB = UK * ROWB;                 // bytes per staging unit
   constexpr int NBUF = kBufBytes / UB < 4 ? kBufBytes / UB : 4;   // units the buffers hold
   constexpr int ROWS_PW = UK / 4;               // key rows each wave stages per unit
   constexpr int PAIRS_PW = UK / 8;              // fp8: DMAs (two key rows each) per wave per unit
-  constexpr int QKB = KS ? 1 : 2;               // 16-key blocks per wave in QK
-  constexpr int QRB = KS ? NRB : 2;             // 16-row blocks per wave in QK
+  constexpr int QKB = 1;                        // 16-key blocks per wave in QK
+  constexpr int QRB = NRB;                      // 16-row blocks per wave in QK
   constexpr int KK = UK / 32;                   // 32-key MFMA steps per unit in PV
   constexpr int NDT = 8;                        // 16-dim blocks of O per wave
   constexpr int PPITCH = UK * 2 + 16;           // bytes per P row (padding spreads banks)
-  constexpr int NSLOT = KS ? 4 : 1;             // waves contributing to one row's sums
+  constexpr int NSLOT = 4;                      // waves contributing to one row's sums
   static_assert(RT * PPITCH <= kPBytes, "P tile");
 
   extern __shared__ uint4 smem[];
@@ -388,8 +396,8 @@ __global__ __launch_bounds__(256) void attn_kernel(const uint16_t* q, const int3
   const int rows_here = min(RT, a.R - row0);
   const int max_keys = a.P * PG;
   // tile row of this lane's QK row block rb, and the first key of QK key block kb
-  auto qrow = [&](int rb) { return (KS ? 0 : 32 * w) + 16 * rb + i16; };
-  auto qkey = [&](int kb) { return KS ? 16 * w : 16 * kb; };
+  auto qrow = [&](int rb) { return 16 * rb + i16; };
+  auto qkey = [&](int) { return 16 * w; };
 
   // Lane offsets of the DMA of row w + 4i (a key row of a unit, or a Q row):
   // its chunk order is swizzled by (w + 4i) & 15, which takes four values per
@@ -428,19 +436,17 @@ __global__ __launch_bounds__(256) void attn_kernel(const uint16_t* q, const int3
                 (uint32_t)(uintptr_t)(sm_pid + 64 * c));
   }
 
-  // ---- key-split tiles, where every wave needs every Q row, stage Q^T through
-  // the last unit buffer: its address needs only the tile, and it is in LDS
-  // by the time the first unit lands.
+  // ---- every wave needs every Q row (QK splits the keys): Q^T is staged
+  // through the last unit buffer: its address needs only the tile, and it is
+  // in LDS by the time the first unit lands.
   // (an fp8 unit is smaller than a bf16 Q tile: Q then takes the top of the
   // staging area, and units are issued into it only after Q left)
   const uint32_t qb = KV8 ? (uint32_t)(kBufBytes - RT * 1024) : (uint32_t)(NBUF - 1) * UB;
-  if constexpr (KS) {
 #pragma unroll
-    for (int i = 0; i < RT / 4; ++i) {
-      const int r = w + 4 * i;
-      const uint16_t* src = a.q + ((size_t)b * a.R + min(row0 + r, a.R - 1)) * D;
-      dma_row16(src, dvoff[i & 3], lds0 + qb + (uint32_t)r * 1024u);
-    }
+  for (int i = 0; i < RT / 4; ++i) {
+    const int r = w + 4 * i;
+    const uint16_t* src = a.q + ((size_t)b * a.R + min(row0 + r, a.R - 1)) * D;
+    dma_row16(src, dvoff[i & 3], lds0 + qb + (uint32_t)r * 1024u);
   }
   // the rest of the arguments, fetched together while the bounds are in flight
   asm volatile("" ::"s"(a.pool), "s"(a.out_lat), "s"(a.lse), "s"(a.part_o), "s"(a.part_lse), "s"(a.N),
@@ -448,7 +454,7 @@ __global__ __launch_bounds__(256) void attn_kernel(const uint16_t* q, const int3
                : "memory");
   // bounds and table landed in every wave (only this wave's Q DMAs, issued
   // after them, may still be outstanding)
-  wait_vm_barrier(KS ? RT / 4 : 0);
+  wait_vm_barrier(RT / 4);
   const int braw = *(const __attribute__((address_space(3))) int32_t*)(sm_bnd + 4 * lane);
   const int tb = (lane < ntok) ? clampi(braw, 0, max_keys) : 0;
 
@@ -609,24 +615,22 @@ __global__ __launch_bounds__(256) void attn_kernel(const uint16_t* q, const int3
 #pragma unroll
   for (int rb = 0; rb < QRB; ++rb) mpreset[rb] = -INFINITY;
 
-  // row max over the 4 lane groups; for key-split tiles also over the 4 waves
+  // row max over the 4 lane groups and the 4 waves
   auto row_reduce_max = [&](float (&m)[QRB]) {
 #pragma unroll
     for (int rb = 0; rb < QRB; ++rb) {
       m[rb] = fmaxf(m[rb], __shfl_xor(m[rb], 16));
       m[rb] = fmaxf(m[rb], __shfl_xor(m[rb], 32));
     }
-    if constexpr (KS) {
-      if (g == 0) {
+    if (g == 0) {
 #pragma unroll
-        for (int rb = 0; rb < QRB; ++rb) xm[w * RT + qrow(rb)] = m[rb];
-      }
-      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-#pragma unroll
-      for (int rb = 0; rb < QRB; ++rb)
-        m[rb] = fmaxf(fmaxf(xm[qrow(rb)], xm[RT + qrow(rb)]), fmaxf(xm[2 * RT + qrow(rb)], xm[3 * RT + qrow(rb)]));
-      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // xm free again
+      for (int rb = 0; rb < QRB; ++rb) xm[w * RT + qrow(rb)] = m[rb];
     }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+    for (int rb = 0; rb < QRB; ++rb)
+      m[rb] = fmaxf(fmaxf(xm[qrow(rb)], xm[RT + qrow(rb)]), fmaxf(xm[2 * RT + qrow(rb)], xm[3 * RT + qrow(rb)]));
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // xm free again
   };
 
   auto compute_unit = [&](int u, int pass) {
@@ -819,10 +823,7 @@ __global__ __launch_bounds__(256) void attn_kernel(const uint16_t* q, const int3
 
   // ---- the pipeline: NBUF - 1 units in flight ahead of the one computed.
   // A second pass runs only if some row's scores jumped past kMaxJump.
-  // Units in flight ahead of the one computed.  Row-split tiles (32-key
-  // units) keep two, not three: a deeper queue only moves the wait from the
-  // memory counter into the DMA issue, where the wave also stops computing.
-  constexpr int AHEAD = KS ? NBUF - 1 : 2;
+  constexpr int AHEAD = NBUF - 1;
 #pragma nounroll
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
@@ -850,21 +851,8 @@ __global__ __launch_bounds__(256) void attn_kernel(const uint16_t* q, const int3
       ++issued;
       pid_next = pid_of(issued);
     };
-    // Key-split tiles move the staged Q to the registers while unit 0 is in
-    // flight.
-    const bool stage_q = KS && pass == 0;
-    if constexpr (!KS) {
-      if (pass == 0) {
-#pragma unroll
-        for (int rb = 0; rb < QRB; ++rb) {
-          const int r = min(row0 + qrow(rb), a.R - 1);
-          const uint4* qp = reinterpret_cast<const uint4*>(a.q + ((size_t)b * a.R + r) * D);
-#pragma unroll
-          for (int ks = 0; ks < 16; ++ks)
-            qreg[rb][ks] = __builtin_bit_cast(bf16x8, qp[KV8 ? 8 * (ks >> 1) + 2 * g + (ks & 1) : ks * 4 + g]);
-        }
-      }
-    }
+    // The staged Q moves to the registers while unit 0 is in flight.
+    const bool stage_q = pass == 0;
     if (n_units > 0) issue_next();
     if (stage_q) {
       // every wave's Q rows landed (only unit 0's DMAs may be outstanding)
@@ -888,8 +876,8 @@ __global__ __launch_bounds__(256) void attn_kernel(const uint16_t* q, const int3
         }
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // the Q buffer is free again
     } else {
-      // The compiler counts only its own loads (row-split Q, bounds, page
-      // ids), not the staging DMAs.  Draining everything here, where unit 0
+      // The compiler counts only its own loads (bounds, page ids), not the
+      // staging DMAs.  Draining everything here, where unit 0
       // has to land anyway, leaves it no reason to wait on the memory counter
       // inside the key loop, where such a wait would also stall on the
       // prefetched units.
@@ -949,10 +937,9 @@ __global__ __launch_bounds__(256) void attn_kernel(const uint16_t* q, const int3
     le += __shfl_xor(le, 32);
     if (g == 0) {
       const int row = qrow(rb);
-      const int slot = KS ? w : 0;
-      if (slot == 0) st_m[row] = mref[rb];
-      st_lr[slot * RT + row] = lr;
-      st_le[slot * RT + row] = le;
+      if (w == 0) st_m[row] = mref[rb];
+      st_lr[w * RT + row] = lr;
+      st_le[w * RT + row] = le;
     }
   }
   __syncthreads();
@@ -1028,12 +1015,20 @@ __global__ __launch_bounds__(256) void attn_kernel(const uint16_t* q, const int3
 #ifndef MLA_ROWS_AHEAD
 #define MLA_ROWS_AHEAD 3
 #endif
+#ifndef MLA_ROWS_AHEAD8
+#define MLA_ROWS_AHEAD8 5
+#endif
 #ifndef MLA_QK_CHAINS
 #define MLA_QK_CHAINS 1
 #endif
 // Verify attention over one (request b, KV split s, 128-row tile) work item,
-// bf16 cache, with every wave owning 32 folded rows for the whole
-// computation (wave w: tile rows 32 w .. +31):
+// bf16 or (KV8) fp8 E4M3 cache, with every wave owning 32 folded rows for the
+// whole computation (wave w: tile rows 32 w .. +31).  An fp8 unit is 32 rows
+// of 512 bytes staged in pairs of rows per DMA; K comes from one 16-byte read
+// per key row for two k-steps (Q^T loaded in the same permuted dim order),
+// V^T from the 8-bit transposing read, both converted to bf16 by hardware
+// before their MFMAs; the cache's scale enters the score scale and the
+// normaliser.
 //   S^T = K Q^T     bf16 MFMA 16x16x32; K (16 keys x 32 dims) from LDS by
 //                   ds_read_b128, Q^T of the wave's rows in registers; each
 //                   row masked by its own bound.
@@ -1047,6 +1042,7 @@ __global__ __launch_bounds__(256) void attn_kernel(const uint16_t* q, const int3
 // No P crosses between waves, so the one barrier per unit is the one that
 // releases a staging buffer.  Softmax as in attn_kernel: each row's reference
 // max is fixed on the split's first unit (a second pass runs past kMaxJump).
+template <bool KV8>
 __global__ __launch_bounds__(256) void attn_rows_kernel(const uint16_t* q, const int32_t* bt,
                                                         const int32_t* bounds, int B, int S, int row_tiles,
                                                         int T, int H, int R, int P, AttnArgs a) {
@@ -1062,15 +1058,19 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const uint16_t* q, const
   a.P = P;
   constexpr int RT = 128;                 // rows per tile
   constexpr int UK = 32;                  // keys per staging unit
-  constexpr int UB = UK * 1024;           // bytes per staging unit
+  constexpr int ROWB = KV8 ? 512 : 1024;  // LDS bytes per staged key row
+  constexpr int UB = UK * ROWB;           // bytes per staging unit
   constexpr int NBUF = kBufBytes / UB;    // staging units the buffers hold
   constexpr int ROWS_PW = UK / 4;         // key rows each wave stages per unit
+  constexpr int OPS_PW = KV8 ? UK / 8 : ROWS_PW;   // DMA instructions per wave per unit (fp8: row pairs)
   constexpr int ND = 32;                  // 16-dim blocks of a row's O
-  constexpr int AHEAD = MLA_ROWS_AHEAD;   // units in flight ahead of the one computed
-  constexpr int KR = 8;                   // K operands in flight (QK)
+  // units in flight ahead of the one computed (fp8 units are half the bytes)
+  constexpr int AHEAD = KV8 ? MLA_ROWS_AHEAD8 : MLA_ROWS_AHEAD;
+  constexpr int KR = 8;                   // K operands in flight (QK; fp8: raw 16-byte reads, two k-steps each)
+  constexpr int KR8 = 4;
   constexpr int VR = 8;                   // V operands in flight (PV)
   constexpr int SPITCH = 1040;            // staged output row pitch (bytes)
-  static_assert(NBUF == 4 && AHEAD < NBUF, "staging ring");
+  static_assert(NBUF <= 8 && AHEAD < NBUF, "staging ring");
   static_assert(RT * SPITCH <= kBufBytes + kPBytes, "row staging");
 
   extern __shared__ uint4 smem[];
@@ -1179,8 +1179,19 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const uint16_t* q, const
   // row per DMA instruction; wave w stages rows w + 4 i.  Rows past the
   // tile's extent and every row of an out-of-range page id are zero-filled
   // instead (never read from the pool).
+  // fp8 rows: chunk c (16 bytes) of key k (0..31 within the unit) sits at
+  // chunk position c ^ X(k), X(k) = (k & 15) ^ 8 (k >> 4 & 1): the 16 keys of
+  // a K read, and the 8 keys {4g..4g+3, 16+4g..16+4g+3} of a transposing V
+  // read, fall on distinct banks.
+  auto xsw8 = [](int k) { return (k & 15) ^ (8 * ((k >> 4) & 1)); };
+  uint32_t dvoff8[4];   // DMA lane offsets of the pair 2 (w + 4 i), 2 (w + 4 i) + 1
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int k = 2 * (w + 4 * i) + (lane >> 5);
+    dvoff8[i] = (uint32_t)((lane >> 5) * 512 + 16 * ((lane & 31) ^ xsw8(k)));
+  }
   struct Stage {
-    const uint16_t* base;   // the unit's first key row in the pool
+    const uint8_t* base;    // the unit's first key row in the pool
     uint32_t buf;           // LDS byte offset of the unit's buffer
     int valid;              // rows of the unit to fetch
   };
@@ -1194,21 +1205,38 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const uint16_t* q, const
     const int pid = __builtin_amdgcn_readfirstlane(pid_raw);
     const bool pid_ok = (unsigned)pid < (unsigned)a.N;
     st.valid = pid_ok ? n_tile - key0 : 0;
-    st.base = reinterpret_cast<const uint16_t*>(a.pool) + ((size_t)(pid_ok ? pid : 0) * PG + (key0 & 63)) * D;
+    st.base = reinterpret_cast<const uint8_t*>(a.pool) + ((size_t)(pid_ok ? pid : 0) * PG + (key0 & 63)) * ROWB;
     st.buf = (uint32_t)(u % NBUF) * UB;
     return st;
   };
-  auto stage_row = [&](const Stage& st, int i, bool full) {   // key row w + 4 i of the unit
-    const int kap = w + 4 * i;
-    if (full || kap < st.valid)
-      dma_row16(st.base + kap * D, dvoff[i & 3], lds0 + st.buf + (uint32_t)kap * 1024u);
-    else
-      *(lds_u32x4*)(sb + st.buf + kap * 1024 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
+  // bf16: key row w + 4 i of the unit.  fp8: the pair of key rows 2 (w + 4 i)
+  // and 2 (w + 4 i) + 1 in one DMA (lanes 0-31 the first); a pair cut by the
+  // tile's extent fetches its first row with lanes 0-31 alone and zero-fills
+  // the second.
+  auto stage_row = [&](const Stage& st, int i, bool full) {
+    if constexpr (KV8) {
+      const int k0 = 2 * (w + 4 * i);
+      const uint32_t dst = st.buf + (uint32_t)k0 * 512u;
+      if (full || k0 + 1 < st.valid) {
+        dma_row16(st.base + k0 * 512, dvoff8[i], lds0 + dst);
+      } else if (k0 < st.valid) {
+        if (lane < 32) dma_row16(st.base + k0 * 512, dvoff8[i], lds0 + dst);
+        else *(lds_u32x4*)(sb + dst + lane * 16) = u32x4{0u, 0u, 0u, 0u};
+      } else {
+        *(lds_u32x4*)(sb + dst + lane * 16) = u32x4{0u, 0u, 0u, 0u};
+      }
+    } else {
+      const int kap = w + 4 * i;
+      if (full || kap < st.valid)
+        dma_row16(st.base + kap * 1024, dvoff[i & 3], lds0 + st.buf + (uint32_t)kap * 1024u);
+      else
+        *(lds_u32x4*)(sb + st.buf + kap * 1024 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
+    }
   };
   auto stage_ops = [&](const Stage& st) {   // DMA instructions this wave issues for the unit
     int ops = 0;
 #pragma unroll
-    for (int i = 0; i < ROWS_PW; ++i) ops += (w + 4 * i) < st.valid;
+    for (int i = 0; i < OPS_PW; ++i) ops += (KV8 ? 2 * (w + 4 * i) : w + 4 * i) < st.valid;
     return ops;
   };
 
@@ -1225,7 +1253,23 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const uint16_t* q, const
   const uint32_t vrow = (uint32_t)(vkey * 1024 + 16 * (((i16 & 3) >> 1) ^ (vsw & 1)) + 8 * (i16 & 1));
   const int vtsw = vsw >> 1;
 
-  bf16x8 qreg[2][16];   // Q[row wrow(rb)][32 ks + 8 g .. +7]
+  // fp8 K: one 16-byte read of key 16 kb + i16 gives k-steps 2j and 2j+1
+  // (dims 64 j + 16 g .. +7 and +8 .. +15; Q^T is loaded in the same order),
+  // chunk 4 j + g at position (4 j + g) ^ i16 ^ 8 kb:
+  //   8192 kb + 256 (j >> 2) + q8b[(j & 3) ^ 2 kb]
+  uint32_t q8b[4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+    q8b[x] = (uint32_t)(512 * i16 + 64 * (x ^ (i16 >> 2)) + 16 * (g ^ (i16 & 3)));
+  // fp8 V^T of dim block d: lane 2k + h of lane group g addresses key
+  // kap(k) = k < 4 ? 4g + k : 16 + 4g + k - 4, dims 16 d + 8 h .. +7; the
+  // transposing 8-bit read hands lane i16 the eight keys kap(0..7) of dim
+  // 16 d + i16, the key order of the P operand
+  const int v8k = (i16 >> 1) < 4 ? 4 * g + (i16 >> 1) : 16 + 4 * g + (i16 >> 1) - 4;
+  const uint32_t v8row = (uint32_t)(v8k * 512 + 8 * (i16 & 1));
+  const int v8x = xsw8(v8k);
+
+  bf16x8 qreg[2][16];   // Q[row wrow(rb)][32 ks + 8 g .. +7]  (fp8: the permuted k-order above)
   f32x4 o[ND][2];       // o[d][rb][i] = O[row wrow(rb)][dim 16 d + 4 g + i]
   float mref[2], mtrue[2], lround[2], lexact[2], mpreset[2];
   bool jumped = false;
@@ -1240,15 +1284,54 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const uint16_t* q, const
   // half are loaded by k_prime() (for the first half, ahead of the unit's
   // DMA burst, so that their LDS latency passes during it).
   bf16x8 kop[KR];
+  u32x4 kraw[KR8];
   auto load_k = [&](int u, int kb, int ks) {
     const uint32_t kbase = (uint32_t)(u % NBUF) * UB + 16384u * (uint32_t)kb;
     return *(const lds_bf16x8*)(sb + kbase + qkb[ks & 3] + 256 * (ks >> 2));
   };
+  auto load_k8 = [&](int u, int kb, int j) {
+    const uint32_t kbase = (uint32_t)(u % NBUF) * UB + 8192u * (uint32_t)kb + 256u * (uint32_t)(j >> 2);
+    return *(const lds_u32x4*)(sb + kbase + q8b[(j & 3) ^ (2 * kb)]);
+  };
   auto k_prime = [&](int u, int kb) {
+    if constexpr (KV8) {
 #pragma unroll
-    for (int ks = 0; ks < KR - 1; ++ks) kop[ks] = load_k(u, kb, ks);
+      for (int j = 0; j < KR8 - 1; ++j) kraw[j] = load_k8(u, kb, j);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KR - 1; ++ks) kop[ks] = load_k(u, kb, ks);
+    }
+  };
+  // fp8: the same contraction, K converted from the raw reads
+  auto qk_half8 = [&](int u, int kb, f32x4 (&s)[2], auto&& after) {
+    f32x4 acc[2];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j + KR8 - 1 < 8) kraw[(j + KR8 - 1) % KR8] = load_k8(u, kb, j + KR8 - 1);
+      const u32x4 r = kraw[j % KR8];
+      const bf16x8 k0 = fp8x8_to_bf16(r[0], r[1]);
+      const bf16x8 k1 = fp8x8_to_bf16(r[2], r[3]);
+      if (j == 0) {
+        mfma16_vzero(acc[0], k0, qreg[0][0]);
+        mfma16_vzero_nw(acc[1], k0, qreg[1][0]);
+      } else {
+        mfma16_vacc(acc[0], k0, qreg[0][2 * j]);
+        mfma16_vacc_nw(acc[1], k0, qreg[1][2 * j]);
+      }
+      after(2 * j);
+      mfma16_vacc(acc[0], k1, qreg[0][2 * j + 1]);
+      mfma16_vacc_nw(acc[1], k1, qreg[1][2 * j + 1]);
+      after(2 * j + 1);
+    }
+    asm volatile("s_nop 7\n\ts_nop 4" : "+v"(acc[0]), "+v"(acc[1]));
+    s[0] = acc[0];
+    s[1] = acc[1];
   };
   auto qk_half = [&](int u, int kb, f32x4 (&s)[2], auto&& after) {
+    if constexpr (KV8) {
+      qk_half8(u, kb, s, after);
+      return;
+    }
     // MLA_QK_CHAINS accumulator chains per row block (k-step ks feeds chain
     // ks % chains); each chain starts from a zero accumulator input
     constexpr int CH = MLA_QK_CHAINS;
@@ -1323,6 +1406,41 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const uint16_t* q, const
   static_assert(VR == 8, "the first eight V operands fill the ring");
   auto pv = [&](int u, auto&& mid) {
     const uint32_t ub = (uint32_t)(u % NBUF) * UB;
+    if constexpr (KV8) {
+      // raw 8-byte transposing reads (eight keys of one dim), converted to
+      // bf16 right before their MFMAs; VR raw reads in flight
+      auto load_v8 = [&](int d) {
+        const uint32_t off = ub + v8row + 256u * (uint32_t)(d >> 4) + 16u * (uint32_t)((d & 15) ^ v8x);
+        return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(sb + off));
+      };
+      i32x2 vraw[VR];
+      bf16x8 vop[VR];
+#pragma unroll
+      for (int d = 0; d < VR; ++d) vraw[d] = load_v8(d);
+#pragma unroll
+      for (int d = 0; d < VR; ++d) {
+        vop[d] = fp8x8_to_bf16((uint32_t)vraw[d][0], (uint32_t)vraw[d][1]);
+        vraw[d] = load_v8(d + VR);
+        mfma16_acc(o[d][0], vop[d], __builtin_bit_cast(bf16x8, pcur[0]));
+        mid(d);
+        __builtin_amdgcn_sched_barrier(0);   // keep mid(d) between these MFMAs
+      }
+#pragma unroll
+      for (int d = 0; d < VR; ++d) {
+        if (d == 0)   // P of row block 1 was just packed by mid()
+          mfma16_acc(o[d][1], vop[d], __builtin_bit_cast(bf16x8, pcur[1]));
+        else
+          mfma16_acc_nw(o[d][1], vop[d], __builtin_bit_cast(bf16x8, pcur[1]));
+      }
+#pragma unroll
+      for (int d = VR; d < ND; ++d) {
+        const bf16x8 v = fp8x8_to_bf16((uint32_t)vraw[d % VR][0], (uint32_t)vraw[d % VR][1]);
+        if (d + VR < ND) vraw[d % VR] = load_v8(d + VR);
+        mfma16_acc(o[d][0], v, __builtin_bit_cast(bf16x8, pcur[0]));
+        mfma16_acc_nw(o[d][1], v, __builtin_bit_cast(bf16x8, pcur[1]));
+      }
+      return;
+    }
     auto load_v = [&](int d) {
       const uint32_t o0 = ub + vrow + 256u * (uint32_t)(d >> 3) + 32u * (uint32_t)((d & 7) ^ vtsw);
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sb + o0));
@@ -1377,21 +1495,23 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const uint16_t* q, const
       lround[rb] = lexact[rb] = 0.f;
     }
     jumped = false;
-    uint32_t ops_ring = 0;   // DMA count of unit v at bits 8 (v % NBUF)
+    uint64_t ops_ring = 0;   // DMA count of unit v at bits 8 (v % NBUF)
     auto ring_set = [&](int v, int ops) {
       const uint32_t sh = 8u * (uint32_t)(v % NBUF);
-      ops_ring = __builtin_amdgcn_readfirstlane((ops_ring & ~(0xFFu << sh)) | ((uint32_t)ops << sh));
+      const uint64_t r = (ops_ring & ~(0xFFull << sh)) | ((uint64_t)ops << sh);
+      ops_ring = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(r >> 32)) << 32) |
+                 (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)r);
     };
-    auto ring_get = [&](int v) { return (int)((ops_ring >> (8 * (v % NBUF))) & 0xFFu); };
+    auto ring_get = [&](int v) { return (int)((ops_ring >> (8 * (v % NBUF))) & 0xFFull); };
     auto stage_unit = [&](int v, int pid_raw) {
       const Stage st = stage_of(v, pid_raw);
-      if (st.valid >= UK) {   // a whole unit: one DMA per row, no per-row test
+      if (st.valid >= UK) {   // a whole unit: one DMA per row (pair), no per-row test
 #pragma unroll
-        for (int i = 0; i < ROWS_PW; ++i) stage_row(st, i, true);
-        ring_set(v, ROWS_PW);
+        for (int i = 0; i < OPS_PW; ++i) stage_row(st, i, true);
+        ring_set(v, OPS_PW);
       } else {
 #pragma unroll
-        for (int i = 0; i < ROWS_PW; ++i) stage_row(st, i, false);
+        for (int i = 0; i < OPS_PW; ++i) stage_row(st, i, false);
         ring_set(v, stage_ops(st));
       }
     };
@@ -1401,7 +1521,8 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const uint16_t* q, const
         const int r = min(row0 + wrow(rb), a.R - 1);
         const uint4* qp = reinterpret_cast<const uint4*>(a.q + ((size_t)b * a.R + r) * D);
 #pragma unroll
-        for (int ks = 0; ks < 16; ++ks) qreg[rb][ks] = __builtin_bit_cast(bf16x8, qp[ks * 4 + g]);
+        for (int ks = 0; ks < 16; ++ks)
+          qreg[rb][ks] = __builtin_bit_cast(bf16x8, qp[KV8 ? 8 * (ks >> 1) + 2 * g + (ks & 1) : ks * 4 + g]);
       }
     }
     // units 0 .. AHEAD-1 up front.  The compiler's own loads (Q) drain with
@@ -1419,8 +1540,8 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const uint16_t* q, const
       // unit u staged; iteration u-1 done everywhere (whole units in flight
       // behind it: the common case, without the general wait's branches)
       newer = __builtin_amdgcn_readfirstlane(newer);
-      if (newer == (AHEAD - 1) * ROWS_PW)
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((AHEAD - 1) * ROWS_PW) : "memory");
+      if (newer == (AHEAD - 1) * OPS_PW)
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((AHEAD - 1) * OPS_PW) : "memory");
       else
         wait_vm_barrier(newer);
       // the unit AHEAD past u, into the buffer unit u-1 released (one burst:
@@ -1518,7 +1639,8 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const uint16_t* q, const
   for (int rb = 0; rb < 2; ++rb) {
     const int row = wrow(rb);
     const bool empty = !(lr[rb] > 0.f);   // a visible key contributes P >= 1 (its max set the reference)
-    const float inv = empty ? 0.f : __builtin_amdgcn_rcpf(lr[rb]);
+    // (an fp8 cache's scale multiplies the values here)
+    const float inv = empty ? 0.f : (KV8 ? a.kv_scale * __builtin_amdgcn_rcpf(lr[rb]) : __builtin_amdgcn_rcpf(lr[rb]));
     lds_u8* const rowp = sb + row * SPITCH + 8 * g;
 #pragma unroll
     for (int d = 0; d < ND; ++d) {
@@ -2201,11 +2323,10 @@ int ensure_device() {
     if (ok) {
       const void* attn[] = {reinterpret_cast<const void*>(attn_kernel<0, false>),
                             reinterpret_cast<const void*>(attn_kernel<1, false>),
-                            reinterpret_cast<const void*>(attn_kernel<2, false>),
                             reinterpret_cast<const void*>(attn_kernel<0, true>),
                             reinterpret_cast<const void*>(attn_kernel<1, true>),
-                            reinterpret_cast<const void*>(attn_kernel<2, true>),
-                            reinterpret_cast<const void*>(attn_rows_kernel)};
+                            reinterpret_cast<const void*>(attn_rows_kernel<false>),
+                            reinterpret_cast<const void*>(attn_rows_kernel<true>)};
       bool fail = false;
       for (const void* f : attn)
         fail |= hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kAttnSmemBytes) !=
@@ -2283,8 +2404,7 @@ int run_attention(const mla_verify_params* p, const mla::Plan& pl, const mla_bf1
   };
   if (mode == 0) return kv8 ? go(attn_kernel<0, true>) : go(attn_kernel<0, false>);
   if (mode == 1) return kv8 ? go(attn_kernel<1, true>) : go(attn_kernel<1, false>);
-  if (mode == 2) return kv8 ? go(attn_kernel<2, true>) : go(attn_kernel<2, false>);
-  if (mode == 3 && !kv8) return go(attn_rows_kernel);
+  if (mode == 3) return kv8 ? go(attn_rows_kernel<true>) : go(attn_rows_kernel<false>);
   return MLA_ERR_SHAPE;
 }
 

@@ -4,7 +4,7 @@ import math
 import numpy as np
 import torch
 
-from verify_inputs import LATENT, PAGE, VerifyInputs, f32_to_bf16_bits
+from verify_inputs import FP8_NAN, LATENT, PAGE, VerifyInputs, f32_to_bf16_bits
 
 # acceptance bar for floating-point outputs and LSE
 MAX_ABS = 1e-2
@@ -136,3 +136,22 @@ def rel_l2(a, b):
 
 def sm_scale():
     return 1.0 / math.sqrt(128)
+
+
+def upload_fp8(x, q_latent_bits=None):
+    """Device inputs with the pool as E4M3 codes (uint8), NaN code elsewhere."""
+    dev = torch.device("cuda:0")
+    pool = torch.full((x.pool.num_pages, PAGE, LATENT), int(FP8_NAN), dtype=torch.uint8, device=dev)
+    if x.pool.page_ids.size:
+        ids = torch.from_numpy(x.pool.page_ids.astype(np.int64)).to(dev)
+        pool[ids] = torch.from_numpy(np.ascontiguousarray(x.pool.pages)).to(dev)
+    d = {
+        "pool": pool,
+        "block_table": torch.from_numpy(x.block_table).to(dev),
+        "kv_bounds": torch.from_numpy(x.kv_bounds).to(dev),
+        "w_uv": bf16_tensor(x.w_uv),
+        "gate": bf16_tensor(x.gate),
+    }
+    ql = q_latent_bits if q_latent_bits is not None else x.q_latent
+    d["q_latent"] = bf16_tensor(ql)
+    return d

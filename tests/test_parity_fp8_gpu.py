@@ -12,30 +12,11 @@ import torch
 import oracle
 import speculative_verify_attention_absorbed_amd as mv
 from gpu_util import (assert_close_output, assert_lse, assert_masked_rows_zero, bits_of,
-                      bf16_tensor, f64_of, log, round_bf16, sync)
+                      bf16_tensor, f64_of, log, round_bf16, sync, upload_fp8)
 from probes import needle_case_fp8, needle_expected_fp8
-from verify_inputs import FP8_NAN, LATENT, PAGE, build_inputs, fp8_cache, make_config
+from verify_inputs import build_inputs, fp8_cache, make_config
 
 pytestmark = pytest.mark.gpu
-
-
-def upload_fp8(x, q_latent_bits=None):
-    """Device inputs with the pool as E4M3 codes (uint8), NaN code elsewhere."""
-    dev = torch.device("cuda:0")
-    pool = torch.full((x.pool.num_pages, PAGE, LATENT), int(FP8_NAN), dtype=torch.uint8, device=dev)
-    if x.pool.page_ids.size:
-        ids = torch.from_numpy(x.pool.page_ids.astype(np.int64)).to(dev)
-        pool[ids] = torch.from_numpy(np.ascontiguousarray(x.pool.pages)).to(dev)
-    d = {
-        "pool": pool,
-        "block_table": torch.from_numpy(x.block_table).to(dev),
-        "kv_bounds": torch.from_numpy(x.kv_bounds).to(dev),
-        "w_uv": bf16_tensor(x.w_uv),
-        "gate": bf16_tensor(x.gate),
-    }
-    ql = q_latent_bits if q_latent_bits is not None else x.q_latent
-    d["q_latent"] = bf16_tensor(ql)
-    return d
 
 
 def qlat_bits(x):

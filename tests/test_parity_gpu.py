@@ -10,11 +10,11 @@ import torch
 
 import oracle
 import speculative_verify_attention_absorbed_amd as mv
-from gpu_util import (assert_close_output, assert_lse, assert_masked_rows_zero, bits_of,
+from gpu_util import (assert_close_output, assert_lse, assert_masked_rows_zero, bits_of, upload_fp8,
                       bf16_tensor, f64_of, log, rel_l2, round_bf16, sync, upload,
                       upload_dense_pool)
 from probes import needle_case, needle_expected
-from verify_inputs import build_inputs, make_config, ramp_scores
+from verify_inputs import build_inputs, fp8_cache, make_config, ramp_scores
 
 pytestmark = pytest.mark.gpu
 
@@ -437,14 +437,19 @@ def check_partials_and_combine(x, splits, tile_rows=0):
     """mla_verify_attn_partials: split s of a row is attention over the keys of
     chunk s of its row tile's partition (clipped to the row's token bound);
     mla_verify_lse_combine of those partials gives the same bits as
-    mla_verify_attn with the same split count and tile."""
+    mla_verify_attn with the same split count and tile.  An fp8 cache
+    (x.kv_dtype == "fp8", inputs from verify_inputs.fp8_cache) is uploaded as
+    its codes and decoded by the oracle with its scale."""
     q_bits = oracle_qlat_bits(x)
-    d = upload(x, q_latent_bits=q_bits)
+    fp8 = getattr(x, "kv_dtype", "bf16") == "fp8"
+    d = upload_fp8(x, q_latent_bits=q_bits) if fp8 else upload(x, q_latent_bits=q_bits)
+    kv = dict(kv_dtype=mv.KV_FP8_E4M3, kv_scale=x.kv_scale) if fp8 else {}
+    decode = oracle.kv_decoder("fp8", x.kv_scale) if fp8 else None
     part_o, part_lse = mv.verify_attn_partials(d["q_latent"], d["pool"], d["block_table"],
                                                d["kv_bounds"], x.sm_scale, num_splits=splits,
-                                               tile_rows=tile_rows)
+                                               tile_rows=tile_rows, **kv)
     out, lse = mv.verify_attn(d["q_latent"], d["pool"], d["block_table"], d["kv_bounds"],
-                              x.sm_scale, num_splits=splits, tile_rows=tile_rows)
+                              x.sm_scale, num_splits=splits, tile_rows=tile_rows, **kv)
     b, t, h = x.shape
     comb, comb_lse = mv.verify_lse_combine(part_o, part_lse)
     sync()
@@ -452,7 +457,7 @@ def check_partials_and_combine(x, splits, tile_rows=0):
     assert np.array_equal(comb_lse.cpu().numpy(), lse.cpu().numpy().reshape(-1))
 
     params = mv.VerifyParams.make(b, t, h, x.block_table.shape[1], x.pool.num_pages, x.sm_scale,
-                                  splits, tile_rows=tile_rows)
+                                  splits, tile_rows=tile_rows, **kv)
     tile = mv.verify_tile_rows(params)
     po = f64_of(part_o).reshape(splits, b, t * h, 512)
     pl = part_lse.cpu().numpy().astype(np.float64).reshape(splits, b, t * h)
@@ -460,10 +465,10 @@ def check_partials_and_combine(x, splits, tile_rows=0):
     max_pages = x.block_table.shape[1]
     want_o, want_l, got_o, got_l = [], [], [], []
     n_empty = 0
-    balanced = tile == 128 and getattr(x, "kv_dtype", "bf16") == "bf16" and splits >= 2 and b <= 2000
+    balanced = tile == 128 and splits >= 2 and b <= 2000
     bal = balanced_chunks(x, splits, tile) if balanced else None
     for bi in range(b):
-        c_b, n_b = oracle.request_keys(x.pool, x.block_table, x.kv_bounds, bi)
+        c_b, n_b = oracle.request_keys(x.pool, x.block_table, x.kv_bounds, bi, decode)
         for r0 in range(0, t * h, tile):
             rows = range(r0, min(r0 + tile, t * h))
             # the tile sees the keys up to its own largest bound
@@ -499,20 +504,23 @@ def test_partials_match_oracle_chunks_and_combine_matches_call(cfg, splits, tile
     check_partials_and_combine(make_config(cfg, sharp=True), splits, tile)
 
 
-@pytest.mark.parametrize("splits", [2, 3, 8])
-def test_partials_balanced_chunks_on_128_row_tiles(splits):
-    """128-row tiles on a bf16 cache (64 heads x 8 tokens: four tiles per
-    request): the balanced-chunk partition, with a request that sees
+@pytest.mark.parametrize("splits,kv", [(2, "bf16"), (3, "bf16"), (8, "bf16"), (3, "fp8"),
+                                       (8, "fp8")])
+def test_partials_balanced_chunks_on_128_row_tiles(splits, kv):
+    """128-row tiles (64 heads x 8 tokens: four tiles per request) on a bf16
+    or an fp8 cache: the balanced-chunk partition, with a request that sees
     nothing, a request whose later tokens see nothing (a tile shorter than
-    the request), lengths on and off unit and page edges, and forced split
-    counts that bind the chunk size (2, 3) or not (8)."""
-    log(f"partials, balanced chunks, S={splits}")
+    the request), lengths on and off unit, pair and page edges, and forced
+    split counts that bind the chunk size (2, 3) or not (8)."""
+    log(f"partials, balanced chunks, S={splits}, {kv} cache")
     ctx = np.array([2000, 0, 33, 1500, 64, 4100, 95, 1])
     bounds = (ctx[:, None] - 7 + np.arange(8)[None, :]).clip(0).astype(np.int32)
     bounds[3, 2:] = 0                      # tiles 1..3 of request 3 see nothing
     bounds[6, :4] = 0
     x = build_inputs(batch=len(ctx), heads=64, q_len=8, ctx=ctx, bounds=bounds, seed=77,
                      latent_q=True, q_scale=1536.0)
+    if kv == "fp8":
+        x = fp8_cache(x)
     check_partials_and_combine(x, splits, tile_rows=128)
 
 
