@@ -1302,24 +1302,32 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const uint16_t* q, const
       for (int ks = 0; ks < KR - 1; ++ks) kop[ks] = load_k(u, kb, ks);
     }
   };
-  // fp8: the same contraction, K converted from the raw reads
+  // fp8: the same contraction, K converted from the raw reads one step
+  // ahead of its MFMAs (the conversions of step j+1 run under those of step
+  // j; the empty asm keeps them there), so no MFMA waits for a conversion
   auto qk_half8 = [&](int u, int kb, f32x4 (&s)[2], auto&& after) {
     f32x4 acc[2];
+    bf16x8 kc0 = fp8x8_to_bf16(kraw[0][0], kraw[0][1]);
+    bf16x8 kc1 = fp8x8_to_bf16(kraw[0][2], kraw[0][3]);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (j + KR8 - 1 < 8) kraw[(j + KR8 - 1) % KR8] = load_k8(u, kb, j + KR8 - 1);
-      const u32x4 r = kraw[j % KR8];
-      const bf16x8 k0 = fp8x8_to_bf16(r[0], r[1]);
-      const bf16x8 k1 = fp8x8_to_bf16(r[2], r[3]);
+      const bf16x8 k0 = kc0, k1 = kc1;
+      if (j + 1 < 8) {
+        const u32x4 r = kraw[(j + 1) % KR8];
+        kc0 = fp8x8_to_bf16(r[0], r[1]);
+        kc1 = fp8x8_to_bf16(r[2], r[3]);
+        asm volatile("" : "+v"(kc0), "+v"(kc1));
+      }
       if (j == 0) {
         mfma16_vzero(acc[0], k0, qreg[0][0]);
         mfma16_vzero_nw(acc[1], k0, qreg[1][0]);
       } else {
-        mfma16_vacc(acc[0], k0, qreg[0][2 * j]);
+        mfma16_vacc_nw(acc[0], k0, qreg[0][2 * j]);
         mfma16_vacc_nw(acc[1], k0, qreg[1][2 * j]);
       }
       after(2 * j);
-      mfma16_vacc(acc[0], k1, qreg[0][2 * j + 1]);
+      mfma16_vacc_nw(acc[0], k1, qreg[0][2 * j + 1]);
       mfma16_vacc_nw(acc[1], k1, qreg[1][2 * j + 1]);
       after(2 * j + 1);
     }
@@ -1413,15 +1421,28 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const uint16_t* q, const
         const uint32_t off = ub + v8row + 256u * (uint32_t)(d >> 4) + 16u * (uint32_t)((d & 15) ^ v8x);
         return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(sb + off));
       };
+      // each operand is converted one dim block ahead of its MFMAs
       i32x2 vraw[VR];
       bf16x8 vop[VR];
+      auto cvt_v = [&](int slot) {
+        const bf16x8 v = fp8x8_to_bf16((uint32_t)vraw[slot][0], (uint32_t)vraw[slot][1]);
+        return v;
+      };
 #pragma unroll
       for (int d = 0; d < VR; ++d) vraw[d] = load_v8(d);
+      vop[0] = cvt_v(0);
+      vraw[0] = load_v8(VR);
 #pragma unroll
       for (int d = 0; d < VR; ++d) {
-        vop[d] = fp8x8_to_bf16((uint32_t)vraw[d][0], (uint32_t)vraw[d][1]);
-        vraw[d] = load_v8(d + VR);
-        mfma16_acc(o[d][0], vop[d], __builtin_bit_cast(bf16x8, pcur[0]));
+        if (d + 1 < VR) {
+          vop[d + 1] = cvt_v(d + 1);
+          asm volatile("" : "+v"(vop[d + 1]));
+          vraw[d + 1] = load_v8(d + 1 + VR);
+        }
+        if (d == 0)   // P of row block 0 was just packed
+          mfma16_acc(o[d][0], vop[d], __builtin_bit_cast(bf16x8, pcur[0]));
+        else
+          mfma16_acc_nw(o[d][0], vop[d], __builtin_bit_cast(bf16x8, pcur[0]));
         mid(d);
         __builtin_amdgcn_sched_barrier(0);   // keep mid(d) between these MFMAs
       }
@@ -1432,11 +1453,18 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const uint16_t* q, const
         else
           mfma16_acc_nw(o[d][1], vop[d], __builtin_bit_cast(bf16x8, pcur[1]));
       }
+      // vraw[k] holds dim block VR + k
+      bf16x8 vc = cvt_v(0);
+      vraw[0] = load_v8(2 * VR);
 #pragma unroll
       for (int d = VR; d < ND; ++d) {
-        const bf16x8 v = fp8x8_to_bf16((uint32_t)vraw[d % VR][0], (uint32_t)vraw[d % VR][1]);
-        if (d + VR < ND) vraw[d % VR] = load_v8(d + VR);
-        mfma16_acc(o[d][0], v, __builtin_bit_cast(bf16x8, pcur[0]));
+        const bf16x8 v = vc;
+        if (d + 1 < ND) {
+          vc = cvt_v((d + 1) % VR);
+          asm volatile("" : "+v"(vc));
+          if (d + 1 + VR < ND) vraw[(d + 1) % VR] = load_v8(d + 1 + VR);
+        }
+        mfma16_acc_nw(o[d][0], v, __builtin_bit_cast(bf16x8, pcur[0]));
         mfma16_acc_nw(o[d][1], v, __builtin_bit_cast(bf16x8, pcur[1]));
       }
       return;
