@@ -1068,6 +1068,7 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const uint16_t* q, const
   constexpr int AHEAD = KV8 ? MLA_ROWS_AHEAD8 : MLA_ROWS_AHEAD;
   constexpr int KR = 8;                   // K operands in flight (QK; fp8: raw 16-byte reads, two k-steps each)
   constexpr int KR8 = 4;
+  constexpr int KCARRY = 2;               // bf16: second-half K operands the first half loads
   constexpr int VR = 8;                   // V operands in flight (PV)
   constexpr int SPITCH = 1040;            // staged output row pitch (bytes)
   static_assert(NBUF <= 8 && AHEAD < NBUF, "staging ring");
@@ -1293,13 +1294,14 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const uint16_t* q, const
     const uint32_t kbase = (uint32_t)(u % NBUF) * UB + 8192u * (uint32_t)kb + 256u * (uint32_t)(j >> 2);
     return *(const lds_u32x4*)(sb + kbase + q8b[(j & 3) ^ (2 * kb)]);
   };
-  auto k_prime = [&](int u, int kb) {
+  auto k_prime = [&](int u, int kb, int from = 0) {
     if constexpr (KV8) {
 #pragma unroll
       for (int j = 0; j < KR8 - 1; ++j) kraw[j] = load_k8(u, kb, j);
     } else {
 #pragma unroll
-      for (int ks = 0; ks < KR - 1; ++ks) kop[ks] = load_k(u, kb, ks);
+      for (int ks = 0; ks < KR - 1; ++ks)
+        if (ks >= from) kop[ks] = load_k(u, kb, ks);
     }
   };
   // fp8: the same contraction, K converted from the raw reads one step
@@ -1335,11 +1337,17 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const uint16_t* q, const
     s[0] = acc[0];
     s[1] = acc[1];
   };
+  // (bf16: the first half's last steps also load the second half's first
+  // KCARRY operands into the ring slots they free, so the second half does
+  // not start behind all of their LDS latency; 16 is a multiple of KR, so
+  // step ks of the second half finds its operand in slot ks % KR.  Carrying
+  // more than two keeps too many registers live between the halves.)
   auto qk_half = [&](int u, int kb, f32x4 (&s)[2], auto&& after) {
     if constexpr (KV8) {
       qk_half8(u, kb, s, after);
       return;
     }
+    static_assert(16 % KR == 0, "ring slots continue across the halves");
     // MLA_QK_CHAINS accumulator chains per row block (k-step ks feeds chain
     // ks % chains); each chain starts from a zero accumulator input
     constexpr int CH = MLA_QK_CHAINS;
@@ -1347,6 +1355,8 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const uint16_t* q, const
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) {
       if (ks + KR - 1 < 16) kop[(ks + KR - 1) % KR] = load_k(u, kb, ks + KR - 1);
+      else if (kb == 0 && ks + KR - 1 - 16 < KCARRY)
+        kop[(ks + KR - 1) % KR] = load_k(u, 1, ks + KR - 1 - 16);
       if (ks < CH) {
         mfma16_vzero_nw(acc[0][ks % CH], kop[ks % KR], qreg[0][ks]);
         mfma16_vzero_nw(acc[1][ks % CH], kop[ks % KR], qreg[1][ks]);
@@ -1593,7 +1603,7 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const uint16_t* q, const
       if (first) {
         // every row's reference for the whole item (log2 domain): the maximum
         // over the split's first unit, or the preset of a second pass
-        k_prime(u, 1);
+        k_prime(u, 1, KV8 ? 0 : KCARRY);
         qk_half(u, 1, s1, [](int) {});
         masked(u, 1, s1, sv1);
 #pragma unroll
@@ -1612,7 +1622,7 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const uint16_t* q, const
       } else {
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) mu[rb] = (mref[rb] == -INFINITY) ? 0.f : mref[rb];
-        k_prime(u, 1);
+        k_prime(u, 1, KV8 ? 0 : KCARRY);
         qk_half(u, 1, s1, [&](int ks) { sm_step(0, sv0, ks); });
         masked(u, 1, s1, sv1);
       }
