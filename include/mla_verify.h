@@ -88,7 +88,7 @@ enum mla_verify_status {
   MLA_ERR_ARG = -4,         /* bad sm_scale, num_splits, pool size, or a   */
                             /* pointer that is not 16-byte aligned         */
   MLA_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required  */
-  MLA_ERR_DEVICE = -6,      /* current device is not gfx950                */
+  MLA_ERR_DEVICE = -6,      /* no GPU visible, or the current one is not gfx950 */
   MLA_ERR_HIP = -7          /* a HIP call or kernel launch failed          */
 };
 

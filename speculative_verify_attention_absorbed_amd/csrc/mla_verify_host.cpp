@@ -167,7 +167,7 @@ const char* mla_verify_status_string(int status) {
     case MLA_ERR_DTYPE: return "unsupported KV dtype (attention takes bf16 or fp8 E4M3 latent pages; cache updates take bf16)";
     case MLA_ERR_ARG: return "invalid argument (sm_scale, num_splits, pool/page counts or alignment)";
     case MLA_ERR_WORKSPACE: return "workspace missing or too small (allocation-free call: needs more than its static scratch)";
-    case MLA_ERR_DEVICE: return "current device is not gfx950 (MI355X)";
+    case MLA_ERR_DEVICE: return "no GPU visible, or the current device is not gfx950 (MI355X)";
     case MLA_ERR_HIP: return "HIP runtime or kernel launch error";
     default: return "unknown status";
   }

@@ -2351,7 +2351,9 @@ std::atomic<void*> g_scratch[kMaxDevices];      // device address of `scratch` o
 
 int ensure_device() {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+  const hipError_t got = hipGetDevice(&dev);
+  if (got == hipErrorNoDevice) return MLA_ERR_DEVICE;   // no GPU visible to this process
+  if (got != hipSuccess) return MLA_ERR_HIP;
   if (dev < 0 || dev >= kMaxDevices) return MLA_ERR_DEVICE;
   int st = g_device_state[dev].load(std::memory_order_acquire);
   if (st == 0) {

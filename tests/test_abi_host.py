@@ -185,3 +185,38 @@ def test_tile_rows_forced_and_resolved(lib):
     for t in (32, 64, 128):
         assert mv.verify_workspace_size(good(num_splits=4, tile_rows=t)) == \
             4 * 16 * 8 * 8 * (512 * 2 + 4)
+
+
+def _gpu_visible():
+    """Whether HIP sees any device (counting devices does not start work on one)."""
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+    except OSError:
+        return False
+    n = ctypes.c_int(0)
+    return hip.hipGetDeviceCount(ctypes.byref(n)) == 0 and n.value > 0
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="needs a host with no GPU visible")
+def test_every_compute_entry_point_reports_no_device(lib):
+    """With every argument valid, a host that sees no GPU gets MLA_ERR_DEVICE
+    from every entry point that launches work (the pointers are never used:
+    the device check comes after the host checks and before any launch)."""
+    buf = ctypes.create_string_buffer(1 << 16)
+    a = ctypes.c_void_p((ctypes.addressof(buf) + 255) & ~255)
+    p = ctypes.byref(good(batch=1, q_len=4, num_heads=8, max_pages_per_req=4, num_pool_pages=8))
+    big = ctypes.c_size_t(1 << 30)
+    calls = {
+        "mla_verify_attn": lambda: lib.mla_verify_attn(p, a, a, a, a, a, a, a, big, None),
+        "mla_verify_attn_gated": lambda: lib.mla_verify_attn_gated(p, a, a, a, a, a, a, a, a, a, a, big, None),
+        "mla_verify_attn_gated_noalloc": lambda: lib.mla_verify_attn_gated_noalloc(p, a, a, a, a, a, a, a, a, a,
+                                                                                   None),
+        "mla_verify_attn_partials": lambda: lib.mla_verify_attn_partials(p, a, a, a, a, a, a, None),
+        "mla_verify_lse_combine": lambda: lib.mla_verify_lse_combine(4, 32, a, a, a, a, None),
+        "mla_verify_absorb_q": lambda: lib.mla_verify_absorb_q(p, a, a, a, None),
+        "mla_verify_kv_append": lambda: lib.mla_verify_kv_append(1, 4, 4, 8, a, a, a, a, a, None),
+        "mla_verify_kv_trim": lambda: lib.mla_verify_kv_trim(1, 4, 4, a, a, a, a, a, None),
+    }
+    for name, call in calls.items():
+        assert call() == -6, name   # MLA_ERR_DEVICE
+    assert "no GPU" in mv.status_string(-6)
