@@ -433,7 +433,7 @@ def balanced_chunks(x, splits, tile):
     return out
 
 
-def check_partials_and_combine(x, splits, tile_rows=0):
+def check_partials_and_combine(x, splits, tile_rows=0, requests=None):
     """mla_verify_attn_partials: split s of a row is attention over the keys of
     chunk s of its row tile's partition (clipped to the row's token bound);
     mla_verify_lse_combine of those partials gives the same bits as
@@ -467,7 +467,7 @@ def check_partials_and_combine(x, splits, tile_rows=0):
     n_empty = 0
     balanced = tile == 128 and splits >= 2 and b <= 2000
     bal = balanced_chunks(x, splits, tile) if balanced else None
-    for bi in range(b):
+    for bi in (range(b) if requests is None else requests):
         c_b, n_b = oracle.request_keys(x.pool, x.block_table, x.kv_bounds, bi, decode)
         for r0 in range(0, t * h, tile):
             rows = range(r0, min(r0 + tile, t * h))
@@ -522,6 +522,35 @@ def test_partials_balanced_chunks_on_128_row_tiles(splits, kv):
     if kv == "fp8":
         x = fp8_cache(x)
     check_partials_and_combine(x, splits, tile_rows=128)
+
+
+def test_more_than_2000_requests_take_per_tile_splits_on_128_row_tiles():
+    """Past 2000 requests the 128-row kernel deals per-tile splits instead of
+    balanced chunks: 2001 requests of 72 folded rows (one partial tile each)
+    under S = 3, some seeing nothing.  The call against the oracle on every
+    row; combine == call bit for bit; the page ranges of a sample of requests'
+    partials as the per-tile rule states them."""
+    log("2001 requests x 72 rows, S=3, 128-row tiles: per-tile splits")
+    rng = np.random.default_rng(2001)
+    b, h, t = 2001, 9, 8
+    ctx = rng.integers(1, 200, size=b)
+    bounds = (ctx[:, None] - (t - 1) + np.arange(t)[None, :]).clip(0).astype(np.int32)
+    bounds[::37] = 0                                    # requests that see nothing
+    x = build_inputs(batch=b, heads=h, q_len=t, ctx=ctx, bounds=bounds, seed=2001,
+                     latent_q=True, q_scale=1536.0)
+    params = mv.VerifyParams.make(b, t, h, x.block_table.shape[1], x.pool.num_pages, x.sm_scale, 3)
+    assert mv.verify_tile_rows(params) == 128
+    check_partials_and_combine(x, 3, tile_rows=0, requests=range(0, b, 97))
+    d = upload(x)   # the drawn q_latent
+    out, lse = mv.verify_attn(d["q_latent"], d["pool"], d["block_table"], d["kv_bounds"],
+                              x.sm_scale, num_splits=3)
+    sync()
+    want_o, want_lse = oracle.verify_attention_latent(x.q_latent, x.pool, x.block_table,
+                                                      x.kv_bounds, x.sm_scale)
+    got = f64_of(out)
+    assert_lse(lse.cpu().numpy().astype(np.float64), want_lse, "2001 requests lse")
+    assert_masked_rows_zero(got, want_lse, "2001 requests out_latent")
+    assert_close_output(got, want_o, "2001 requests out_latent")
 
 
 def test_partials_ragged_batch_takes_fewer_splits_for_short_requests():
