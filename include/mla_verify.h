@@ -187,8 +187,8 @@ int mla_verify_attn(const mla_verify_params* p,
  * tr = mla_verify_tile_rows(p, 0) rows (the last tile of a request may be
  * partial); a tile sees the keys below L, the largest bound among the tokens
  * of its rows.
- *  - Tiles of 128 rows (bf16 or fp8 cache) with S >= 2 and B <= 2000 (balanced
- *    chunks): request b has U_b = ceil(n_b / 32) units of 32 keys, n_b its
+ *  - Tiles of 128 rows (bf16 or fp8 cache) with S >= 2, B <= 2000 and P <= 1024
+ *    (balanced chunks): request b has U_b = ceil(n_b / 32) units of 32 keys, n_b its
  *    largest bound, and occupies V_b = U_b + F positions (F =
  *    MLA_VERIFY_ITEM_UNITS; V_b = 0 when U_b = 0): F for its start-up, then
  *    its units.  The requests laid end to end (request b at position

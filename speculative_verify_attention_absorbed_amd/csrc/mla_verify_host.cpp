@@ -99,8 +99,12 @@ Plan make_plan(const mla_verify_params* p, bool gated) {
   pl.use_partials = gated || s > 1;
   // 128-row tiles with a split count: balanced chunks.  A request of at
   // most 2 P units spans at most floor((2P - 1) / C) + 2 chunks, which is <= S
-  // once C >= ceil(2P / (S - 1)).
-  pl.balanced = pl.shape.mode == 3 && s >= 2 && p->batch <= kMaxBalancedBatch;
+  // once C >= ceil(2P / (S - 1)).  A chunk can hold more pages of one request
+  // than a workgroup stages block-table entries, so balanced chunks need the
+  // whole block-table row to fit (P <= kMaxSplitPages); longer rows take the
+  // per-tile splits, whose page count per split the argument check bounds.
+  pl.balanced = pl.shape.mode == 3 && s >= 2 && p->batch <= kMaxBalancedBatch &&
+                p->max_pages_per_req <= kMaxSplitPages;
   pl.chunk_min = pl.balanced ? (2 * p->max_pages_per_req + s - 2) / (s - 1) : 0;
   const size_t total_rows = (size_t)p->batch * pl.rows;
   // partial outputs in bf16, partial LSEs in fp32

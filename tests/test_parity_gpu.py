@@ -465,7 +465,7 @@ def check_partials_and_combine(x, splits, tile_rows=0, requests=None):
     max_pages = x.block_table.shape[1]
     want_o, want_l, got_o, got_l = [], [], [], []
     n_empty = 0
-    balanced = tile == 128 and splits >= 2 and b <= 2000
+    balanced = tile == 128 and splits >= 2 and b <= 2000 and max_pages <= 1024
     bal = balanced_chunks(x, splits, tile) if balanced else None
     for bi in (range(b) if requests is None else requests):
         c_b, n_b = oracle.request_keys(x.pool, x.block_table, x.kv_bounds, bi, decode)
@@ -551,6 +551,31 @@ def test_more_than_2000_requests_take_per_tile_splits_on_128_row_tiles():
     assert_lse(lse.cpu().numpy().astype(np.float64), want_lse, "2001 requests lse")
     assert_masked_rows_zero(got, want_lse, "2001 requests out_latent")
     assert_close_output(got, want_o, "2001 requests out_latent")
+
+
+@pytest.mark.parametrize("splits", [0, 2, 3])
+def test_long_block_table_row_on_128_row_tiles(splits):
+    """A block-table row longer than a workgroup stages (70000 keys = 1094
+    pages) with 72 folded rows per request: the 128-row kernel takes per-tile
+    splits, each staging its own slice of the row.  The call against the
+    oracle; with S = 2 and 3, also the partials over the per-tile page ranges
+    and their combine against the call."""
+    log(f"long block-table row, 72 rows, 128-row tiles, S={splits}")
+    x = build_inputs(batch=2, heads=9, q_len=8, ctx=np.array([70000, 3000]), seed=43,
+                     latent_q=True, q_scale=1536.0)
+    assert x.block_table.shape[1] > 1024
+    d = upload(x)
+    out, lse = mv.verify_attn(d["q_latent"], d["pool"], d["block_table"], d["kv_bounds"],
+                              x.sm_scale, num_splits=splits)
+    sync()
+    want_o, want_lse = oracle.verify_attention_latent(x.q_latent, x.pool, x.block_table,
+                                                      x.kv_bounds, x.sm_scale)
+    got = f64_of(out)
+    assert_lse(lse.cpu().numpy().astype(np.float64), want_lse, f"long row S{splits} lse")
+    assert_close_output(got, want_o, f"long row S{splits} out_latent")
+    if splits:
+        del d
+        check_partials_and_combine(x, splits, tile_rows=128)
 
 
 def test_partials_ragged_batch_takes_fewer_splits_for_short_requests():
