@@ -14,7 +14,7 @@ from gpu_util import (assert_close_output, assert_lse, assert_masked_rows_zero, 
                       bf16_tensor, f64_of, log, rel_l2, round_bf16, sync, upload,
                       upload_dense_pool)
 from probes import needle_case, needle_expected
-from verify_inputs import build_inputs, fp8_cache, make_config, ramp_scores
+from verify_inputs import SHARP_Q_SCALE, build_inputs, fp8_cache, make_config, ramp_scores
 
 pytestmark = pytest.mark.gpu
 
@@ -328,6 +328,22 @@ def test_gated_parity(cfg, splits, tile):
     q_bits = oracle_qlat_bits(x)
     d = upload(x, q_latent_bits=q_bits)
     check_gated(x, d, q_bits, num_splits=splits, what=f"cfg{cfg}", tile_rows=tile)
+
+
+@pytest.mark.parametrize("splits,heads", [(24, 8), (64, 8), (24, 9), (64, 9)])
+def test_gated_many_splits(splits, heads):
+    """More than 16 splits per row, so the gated epilogue takes 32 or 64
+    lanes per row: 64 folded rows (two 32-row tiles) and 72 (one 128-row
+    tile), a 20000-key request beside a short one and one that sees
+    nothing."""
+    log(f"gated parity: S={splits}, H={heads}, T=8, ctx (20000, 3000, 0)")
+    ctx = np.array([20000, 3000, 0])
+    bounds = (ctx[:, None] - 7 + np.arange(8)[None, :]).clip(0).astype(np.int32)
+    x = build_inputs(batch=3, heads=heads, q_len=8, ctx=ctx, bounds=bounds, seed=61,
+                     q_scale=SHARP_Q_SCALE)
+    q_bits = oracle_qlat_bits(x)
+    d = upload(x, q_latent_bits=q_bits)
+    check_gated(x, d, q_bits, num_splits=splits, what=f"S{splits} H{heads}")
 
 
 @pytest.mark.parametrize("batch,q_len,heads", [(5, 14, 3), (13, 10, 128)])
